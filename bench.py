@@ -1,0 +1,247 @@
+"""Benchmark: one chunk of query-oriented sparse KV selection + attention over
+the selected keys, on one MI355X.
+
+A step is the whole hot path over one chunk whose inputs are resident in HBM:
+    qk_qsel -> qk_kvscore -> qk_topk -> qk_sparse_attn_indexed
+(the gather of the selected rows is fused into the attention's loads).
+Steps rotate over several copies of the inputs (more bytes than the 256 MB
+Infinity Cache), so each step streams its K and V from HBM.
+
+Prints one JSON line.  `value` is the chunk latency in ms (the metric's unit;
+lower is better).  `roofline` covers the kernel that dominates the step;
+`roofline_scoring` covers the scoring pass (the metric's GB/s half).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_kv_selection_amd as qk  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "selected-KV attention chunk ms @T=32K + scoring HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+
+
+def _describe(s) -> str:
+    return (f"b={s.b} nq={s.nq} nkv={s.nkv} d={s.d} T={s.t_past} bcp={s.bcp} "
+            f"NQ={s.nq_keep} BSA={s.bsa}" + (f" rounds={s.n_rounds} top={s.top_rounds}+latest"
+                                             if s.n_rounds else ""))
+
+
+def algorithmic(spec, n_sel_per_bj):
+    """Per-step algorithmic work.  n_sel_per_bj: mean selected past keys per
+    (sequence, KV head)."""
+    esz = 2 if spec.dtype == "bf16" else 4
+    bnkv = spec.b * spec.nkv
+    # scoring: every past key read once (d*esz) + one fp32 score written, plus the group queries
+    score_bytes = bnkv * spec.t_past * (spec.d * esz + 4) + bnkv * spec.nq_keep * spec.d * 4
+    score_flops = 2.0 * bnkv * spec.nq_keep * spec.d * spec.t_past
+    # attention: 4*d flops per (query row, attended key); causal chunk counts its half
+    rows = spec.b * spec.nq * spec.bcp
+    causal_pairs = spec.b * spec.nq * spec.bcp * (spec.bcp + 1) / 2
+    attn_flops = 4.0 * spec.d * (rows * n_sel_per_bj + causal_pairs)
+    attn_bytes = (bnkv * n_sel_per_bj * 2 * spec.d * esz + bnkv * spec.bcp * 2 * spec.d * esz
+                  + 2 * rows * spec.d * esz)
+    dense_flops = 4.0 * spec.d * (rows * spec.t_past + causal_pairs)
+    return dict(score_bytes=score_bytes, score_flops=score_flops, attn_flops=attn_flops,
+                attn_bytes=attn_bytes, dense_flops=dense_flops)
+
+
+def cpu_baseline(spec, seed, budget_s: float):
+    """The fp64 oracle, as it stands, on this host: the full chunk if it fits
+    the time budget, else a row sample of the attention (selection is always
+    complete) scaled to one chunk."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    case = W.make_case(spec, seed)
+    qn = case["q"].float().numpy().astype(np.float64)
+    kn = case["k"].float().numpy().astype(np.float64)
+    vn = case["v"].float().numpy().astype(np.float64)
+    off = case["round_off"].numpy() if case["round_off"] is not None else None
+    t0 = time.perf_counter()
+    sel = oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, round_off=off,
+                          top_rounds=spec.top_rounds, with_attention=False)
+    t_sel = time.perf_counter() - t0
+    # time attention on growing row samples until the budget is used, then scale
+    rows_total = spec.bcp
+    n = max(1, min(rows_total, 8))
+    t_att, done = 0.0, 0
+    rng = np.random.default_rng(seed)
+    while True:
+        rows = np.sort(rng.choice(rows_total, n, replace=False))
+        t1 = time.perf_counter()
+        oracle.attention(qn, kn, vn, spec.t_past, sel["key_sets"], rows=rows)
+        dt = time.perf_counter() - t1
+        t_att, done = dt, n
+        if n == rows_total or t_sel + dt * 4 > budget_s:
+            break
+        n = min(rows_total, n * 4)
+    est = t_sel + t_att * rows_total / done
+    sample = (f"full selection (all {spec.b * spec.nkv} KV heads, T={spec.t_past}) + attention "
+              f"of {done}/{rows_total} chunk rows x all {spec.nq} heads"
+              + ("" if done == rows_total else ", scaled to the whole chunk"))
+    return {"value": est * 1e3, "unit": "ms per chunk", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "host": platform.processor() or platform.machine(),
+            "selection_ms": t_sel * 1e3, "measured_s": t_sel + t_att}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3b_32k", choices=sorted(W.CONFIGS))
+    ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated over (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--gathered", action="store_true", help="qk_gather + qk_sparse_attn instead of the fused path")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each KV head or sequence would shard with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spec = W.spec(args.workload)
+    rounds = spec.n_rounds > 0
+    shape = qk.shape_of(spec, bsa=spec.t_past // 4 if rounds else spec.bsa)
+    one_copy = sum(spec.b * h * r * spec.d * (2 if spec.dtype == "bf16" else 4)
+                   for h, r in ((spec.nq, spec.bcp), (spec.nkv, spec.kv_cap), (spec.nkv, spec.kv_cap)))
+    copies = args.copies or max(2, min(16, int(np.ceil(1.0e9 / one_copy))))
+    inputs = []
+    for c in range(copies):
+        case = W.make_case(spec, args.seed + 7919 * c, device=dev)
+        inputs.append(case)
+    pipe = qk.Pipeline(shape, device=dev, n_rounds=spec.n_rounds, top_rounds=spec.top_rounds,
+                       fused_gather=not args.gathered)
+    torch.cuda.synchronize()
+
+    def step(i):
+        c = inputs[i % copies]
+        pipe.select(c["q"], c["k"], c["round_off"])
+        pipe.attend(c["q"], c["k"], c["v"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-stage durations on the same stream (events between the calls)
+    stages = ["qsel", "kvscore", "select", "attention"]
+    acc = {s: 0.0 for s in stages}
+    reps = max(10, args.steps)
+    for i in range(reps):
+        c = inputs[i % copies]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record()
+        qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
+        ev[1].record()
+        qk.qk_kvscore(shape, pipe.q_group, c["k"], pipe.s_agg)
+        ev[2].record()
+        if rounds:
+            qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"], spec.top_rounds,
+                               True, pipe.idx, pipe.ld_idx, pipe.sel_len, pipe.s_round)
+        else:
+            qk.qk_topk(shape.b * shape.nkv, shape.t_past, shape.bsa, pipe.s_agg, shape.t_past,
+                       pipe.idx, pipe.ld_idx)
+        ev[3].record()
+        pipe.attend(c["q"], c["k"], c["v"])
+        ev[4].record()
+        torch.cuda.synchronize()
+        for si, s in enumerate(stages):
+            acc[s] += ev[si].elapsed_time(ev[si + 1])
+    stage_ms = {s: acc[s] / reps for s in stages}
+
+    n_sel = float(pipe.sel_len.float().mean()) if rounds else float(shape.n_sel)
+    work = algorithmic(spec, n_sel)
+    score_gbs = work["score_bytes"] / (stage_ms["kvscore"] * 1e-3) / 1e9
+    attn_tflops = work["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
+    roof_score = {"kernel": "qk_kvscore", "bound": "hbm", "achieved": round(score_gbs, 1),
+                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                  "traffic": None, "algorithmic_bytes": work["score_bytes"],
+                  "ms": round(stage_ms["kvscore"], 5)}
+    if spec.bcp == 1:
+        attn_gbs = work["attn_bytes"] / (stage_ms["attention"] * 1e-3) / 1e9
+        roof_attn = {"kernel": "qk_sparse_attn_indexed", "bound": "hbm", "achieved": round(attn_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": work["attn_bytes"],
+                     "ms": round(stage_ms["attention"], 5)}
+    else:
+        roof_attn = {"kernel": "qk_sparse_attn_indexed", "bound": "mfma", "achieved": round(attn_tflops, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": work["attn_flops"], "ms": round(stage_ms["attention"], 5)}
+    dominant = roof_attn if stage_ms["attention"] >= stage_ms["kvscore"] else roof_score
+
+    result = {
+        "metric": METRIC, "value": round(ms, 5), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: {_describe(spec)}", "input_copies": copies,
+                   "gather": "gathered" if args.gathered else "fused into attention"},
+        "roofline": dominant, "roofline_scoring": roof_score, "roofline_attention": roof_attn,
+        "scoring_gbps": round(score_gbs, 1), "scoring_frac_of_peak": round(score_gbs / HBM_PEAK_GBS, 4),
+        "keys_scored_per_s": spec.b * spec.nkv * spec.t_past / (stage_ms["kvscore"] * 1e-3),
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "chunks_per_s": round(1e3 / ms, 1),
+    }
+
+    if not args.no_dense:
+        dout = torch.empty_like(inputs[0]["q"])
+        nws = qk.qk_workspace_bytes(shape, "dense_attn")
+        dws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            c = inputs[i % copies]
+            qk.qk_dense_attn(shape, c["q"], c["k"], c["v"], dout, None, dws, nws)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nd = max(5, args.steps // 5)
+        d0.record()
+        for i in range(nd):
+            c = inputs[i % copies]
+            qk.qk_dense_attn(shape, c["q"], c["k"], c["v"], dout, None, dws, nws)
+        d1.record()
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / nd
+        result["dense_attention_ms"] = round(dms, 5)
+        result["dense_attention_tflops"] = round(work["dense_flops"] / (dms * 1e-3) / 1e12, 1)
+        result["chunk_vs_dense_attention"] = round(dms / ms, 3)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, args.seed, args.cpu_budget)
+        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * qk.h -- C ABI of the query-oriented sparse KV selection library (gfx950).
+ *
+ * One prefill chunk (or one decode token) of attention with QUOKA-style key
+ * selection:
+ *
+ *   qk_qsel         mean query, negated cosine scores, top-NQ queries per head,
+ *                   normalise and average over each GQA group
+ *   qk_kvscore      cosine score of every past key against the group queries,
+ *                   max over the kept queries
+ *   qk_topk         per-row top-k indices of fp32 scores (ascending order)
+ *   qk_round_select round-granular variant: round score = max over the round,
+ *                   keep the latest round plus the top rounds
+ *   qk_gather       copy the selected K/V rows into dense buffers
+ *   qk_sparse_attn  softmax attention of the chunk over gathered selected keys
+ *                   (no mask) plus the chunk's own keys (causal)
+ *   qk_sparse_attn_indexed  same, reading the selected rows straight from the
+ *                   cache through the index list (gather fused into the loads)
+ *   qk_dense_attn   the same chunk over every past key (reference path)
+ *
+ * Sources: the "QUOKA" technical write-up (bqwf.cn) -- section 2.1 Algorithm 1
+ * (query sub-selection), section 2.2 (cosine score S_ij), section 2.3
+ * (aggregation listing), section 4.2 question 3 (the selected KV is the
+ * attention's KV input, causal mask disabled); the Round Attention press
+ * release (Moore Threads), sections 01-02 (round-granular block top-K).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers are DEVICE pointers unless marked [host].  Tensors are row-major and
+ * contiguous:
+ *     q        (b, nq,  bcp,    d)     the chunk's queries (bcp = 1: decode)
+ *     k, v     (b, nkv, kv_cap, d)     rows [0, t_past) are the past,
+ *                                      rows [t_past, t_past + bcp) the chunk's own
+ *     out      (b, nq,  bcp,    d)     same dtype as q
+ *     q_group  (b, nkv, nq_keep, d)    fp32
+ *     s_agg    (b, nkv, t_past)        fp32
+ *     idx      (b, nkv, ld_idx)        int32 past positions
+ * Query head h uses KV head h / (nq / nkv).
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer past
+ * return and allocates nothing.  Outputs must not alias inputs.  Scratch memory
+ * comes from the caller as (ws, ws_bytes), sized by qk_workspace_bytes.
+ *
+ * Execution: every call validates its arguments on the host, enqueues its
+ * kernels on `stream` and returns without synchronising.  The library holds no
+ * mutable global state; calls on different streams are independent.
+ *
+ * Errors: validation happens before any launch; on error nothing is launched
+ * and nothing is written.  A failed launch returns QK_ERR_HIP.  Faults inside a
+ * kernel surface at the caller's next synchronisation.  Inputs must be finite.
+ */
+#ifndef QK_H_
+#define QK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* qk_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  QK_OK = 0,
+  QK_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  QK_ERR_SHAPE = 2,       /* a size is out of range or inconsistent           */
+  QK_ERR_DTYPE = 3,       /* dtype not supported by this call                 */
+  QK_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned          */
+  QK_ERR_WORKSPACE = 5,   /* ws_bytes smaller than qk_workspace_bytes         */
+  QK_ERR_UNSUPPORTED = 6, /* head dim or size beyond what the kernels handle  */
+  QK_ERR_HIP = 7          /* the HIP runtime refused a launch                 */
+} qk_status;
+
+typedef enum { QK_F32 = 0, QK_BF16 = 1 } qk_dtype;
+
+/* [host] Problem description shared by the calls. */
+typedef struct {
+  int32_t b;        /* sequences in the batch, >= 1                              */
+  int32_t nq;       /* query heads, a multiple of nkv                            */
+  int32_t nkv;      /* KV heads, >= 1                                            */
+  int32_t d;        /* head dim: 64, 128 or 256                                  */
+  int32_t bcp;      /* chunk queries, 1 .. 8192 (1 = decode)                     */
+  int32_t t_past;   /* T, past positions scored, >= 0 (>= 1 for selection)        */
+  int32_t kv_cap;   /* rows per (sequence, KV head) in k and v, >= t_past + bcp  */
+  int32_t nq_keep;  /* NQ, kept queries per head, 1 .. min(bcp, 256)             */
+  int32_t bsa;      /* BSA, kept keys per KV head, >= 1; values above T act as T */
+  float scale;      /* softmax scale; 0 means 1/sqrt(d)                          */
+  int32_t dtype;    /* qk_dtype of q, k, v and out                               */
+} qk_shape;
+
+/* Operation codes for qk_workspace_bytes. */
+typedef enum {
+  QK_OP_QSEL = 0,
+  QK_OP_KVSCORE = 1,
+  QK_OP_TOPK = 2,
+  QK_OP_ROUND_SELECT = 3,
+  QK_OP_GATHER = 4,
+  QK_OP_SPARSE_ATTN = 5,
+  QK_OP_DENSE_ATTN = 6
+} qk_op;
+
+/* [host] Version of this ABI (bumped on any incompatible change). */
+int32_t qk_abi_version(void);
+
+/* [host] Text for a status code; never NULL. */
+const char* qk_status_string(qk_status s);
+
+/* [host] Scratch bytes `op` needs for shape `s` (0 if none).  For QK_OP_TOPK,
+ * s->b is read as the row count and s->t_past as the row length.  For the
+ * attention ops with a ragged selection (sel_len != NULL), s->bsa must be the
+ * largest selection length.  Returns 0 for an invalid shape. */
+size_t qk_workspace_bytes(const qk_shape* s, int32_t op);
+
+/* Query sub-selection and group aggregation (QUOKA write-up, section 2.1
+ * Algorithm 1 and section 2.3 listing).
+ *   MQ[b,h]  = mean over the chunk of q[b,h,i]
+ *   SQ[b,h,i] = -(q.MQ) / (max(|q|,1e-12) max(|MQ|,1e-12))
+ *   q_idx[b,h,0..NQ) = positions of the NQ largest SQ, largest first (ties:
+ *                      lower position)
+ *   q_group[b,j,n] = mean over g < G of q[b,jG+g,q_idx[b,jG+g,n]] / |.|
+ * q: (b,nq,bcp,d) f32 or bf16.  q_idx: (b,nq,NQ) int32.  sq: (b,nq,bcp) f32 or
+ * NULL.  q_group: (b,nkv,NQ,d) f32.  Arithmetic is fp32. */
+qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq,
+                  float* q_group, qk_stream_t stream);
+
+/* Key scoring (QUOKA write-up, section 2.2 S_ij and section 2.3 listing).
+ *   s_agg[b,j,t] = max over n < NQ of q_group[b,j,n].k[b,j,t] / max(|k[b,j,t]|,1e-12)
+ * for t < T.  k: (b,nkv,kv_cap,d) f32 or bf16.  Reads every past key once.
+ * bf16: products on the matrix cores with q_group split into a bf16 high and
+ * low part (about 2^-16 relative), fp32 accumulation.  f32: fp32 FMA. */
+qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k,
+                     float* s_agg, qk_stream_t stream);
+
+/* Per-row top-k of fp32 scores (QUOKA write-up, section 2.3: top-BSA keys per
+ * KV head).  scores: (rows, n), row stride ld_scores >= n.  idx: (rows, k)
+ * int32, row stride ld_idx >= k: the k positions with the largest score (ties:
+ * lower position; -0.0 equals +0.0), in ascending position order.  k > n acts
+ * as n; positions k..ld_idx of each row are left untouched.  Needs
+ * qk_workspace_bytes(QK_OP_TOPK) of scratch (currently none). */
+qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores,
+                  int32_t ld_scores, int32_t* idx, int32_t ld_idx, void* ws,
+                  size_t ws_bytes, qk_stream_t stream);
+
+/* Round-granular selection (Round Attention press release, sections 01-02).
+ * round_off: (n_rounds + 1) int32, off[0] = 0, strictly increasing,
+ * off[n_rounds] = t_past.  For each (b, KV head):
+ *   s_round[r] = max over off[r] <= t < off[r+1] of s_agg[b,j,t]
+ *   chosen     = {n_rounds-1} and the top_r best of the other rounds when
+ *                keep_latest != 0 (else the top_r best of all); ties: lower id
+ *   idx[b,j,0..sel_len) = every position of the chosen rounds, ascending
+ * idx: (b,nkv,ld_idx) int32 with ld_idx >= the largest possible selection
+ * (t_past is always enough); sel_len: (b,nkv) int32; s_round: (b,nkv,n_rounds)
+ * f32 or NULL.  1 <= top_r, top_r + (keep_latest != 0) <= n_rounds <= 4096. */
+qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,
+                          const int32_t* round_off, int32_t top_r,
+                          int32_t keep_latest, int32_t* idx, int32_t ld_idx,
+                          int32_t* sel_len, float* s_round, qk_stream_t stream);
+
+/* Gather the selected rows (QUOKA write-up, section 4.2 question 3: the
+ * selection is the attention's KV input).
+ *   k_sel[b,j,r] = k[b,j,idx[b,j,r]], v_sel likewise, for r < n_sel(b,j)
+ * n_sel = sel_len[b,j] if sel_len != NULL, else min(bsa, t_past).
+ * idx: (b,nkv,ld_idx); k_sel, v_sel: (b,nkv,ld_idx,d) same dtype as k.
+ * Every index must lie in [0, t_past). */
+qk_status qk_gather(const qk_shape* s, const void* k, const void* v,
+                    const int32_t* idx, int32_t ld_idx, const int32_t* sel_len,
+                    void* k_sel, void* v_sel, qk_stream_t stream);
+
+/* Attention over the selected keys (QUOKA write-up, section 4.2 question 3).
+ * For query head h (KV head j) and chunk row i, the keys are the n_sel rows of
+ * (k_sel, v_sel)[b,j] -- all visible -- and the chunk rows t_past + u of (k, v)
+ * for u <= i.
+ *   out[b,h,i] = sum_key softmax(scale q.key) value;  lse = log sum exp(scale q.key)
+ * k_sel, v_sel: (b,nkv,ld_sel,d); sel_len as in qk_gather; lse: (b,nq,bcp) f32
+ * or NULL.  bf16: matrix-core products, fp32 softmax and accumulation; f32:
+ * fp32 throughout.  Scratch: qk_workspace_bytes(QK_OP_SPARSE_ATTN). */
+qk_status qk_sparse_attn(const qk_shape* s, const void* q, const void* k_sel,
+                         const void* v_sel, int32_t ld_sel, const int32_t* sel_len,
+                         const void* k, const void* v, void* out, float* lse,
+                         void* ws, size_t ws_bytes, qk_stream_t stream);
+
+/* As qk_sparse_attn, but the selected past keys are read from the cache
+ * through idx (b,nkv,ld_idx) -- the gather is fused into the attention's tile
+ * loads and no k_sel / v_sel copy is made.  Every index must lie in
+ * [0, t_past). */
+qk_status qk_sparse_attn_indexed(const qk_shape* s, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t ld_idx,
+                                 const int32_t* sel_len, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, qk_stream_t stream);
+
+/* Dense attention of the chunk over every past key plus itself causally (the
+ * dense baseline of the QUOKA write-up's section 3 tables).  Same outputs and
+ * scratch rules as qk_sparse_attn (op QK_OP_DENSE_ATTN). */
+qk_status qk_dense_attn(const qk_shape* s, const void* q, const void* k,
+                        const void* v, void* out, float* lse, void* ws,
+                        size_t ws_bytes, qk_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H_ */

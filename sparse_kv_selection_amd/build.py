@@ -1,0 +1,66 @@
+"""Build the HIP library in-tree: hipcc for gfx950 -> sparse_kv_selection_amd/libqk.so.
+
+Objects go to _build/ at the repository root; the shared library is written
+next to this file so that it travels with the source tree.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libqk.so")
+BUILD = os.path.join(ROOT, "_build")
+
+SOURCES = ["api.hip", "qsel.hip", "kvscore.hip", "topk.hip", "gather_rounds.hip", "attention.hip"]
+
+ARCH = os.environ.get("QK_OFFLOAD_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # packed fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mcode-object-version=5",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libqk.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)

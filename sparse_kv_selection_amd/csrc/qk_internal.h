@@ -1,0 +1,54 @@
+// Host-side launchers of the kernels, called by the C ABI after validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+// Query sub-selection + group aggregation.
+hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group,
+                       int b, int nq, int nkv, int d, int bcp, int nq_keep, hipStream_t st);
+
+// Key scoring pass.
+hipError_t launch_kvscore(bool bf16, const float* q_group, const void* k, float* s_agg, int b,
+                          int nkv, int d, int t_past, int kv_cap, int nq_keep, hipStream_t st);
+
+// Per-row top-k, ascending indices.
+hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
+                       int ld_idx, hipStream_t st);
+
+// Round scores, selection and ragged expansion.
+hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,
+                               const int32_t* off, int top_r, int keep_latest, int32_t* idx,
+                               int ld_idx, int32_t* sel_len, float* s_round, hipStream_t st);
+
+// Row gather of selected K/V rows.
+hipError_t launch_gather(int esz, const void* k, const void* v, const int32_t* idx, int ld_idx,
+                         const int32_t* sel_len, int n_sel, void* k_sel, void* v_sel, int bnkv,
+                         int d, int kv_cap, hipStream_t st);
+
+// Attention over past rows (gathered, indexed or contiguous) plus the causal chunk.
+struct AttnCall {
+  bool bf16;
+  const void* q;
+  const void* pk;           // past key rows
+  const void* pv;           // past value rows
+  long long past_bj_rows;   // rows between consecutive (b, kv head) blocks of pk / pv
+  const int32_t* idx;       // past row list per (b, kv head) or nullptr (identity)
+  int ld_idx;
+  const int32_t* sel_len;   // per (b, kv head) past count, or nullptr
+  int n_past;               // past count when sel_len is nullptr; upper bound otherwise
+  const void* k;            // cache (chunk rows read at t_past + u)
+  const void* v;
+  int kv_cap, t_past;
+  void* out;
+  float* lse;
+  void* ws;
+  int b, nq, nkv, d, bcp;
+  float scale;
+};
+size_t attn_workspace_bytes(bool bf16, int b, int nq, int nkv, int d, int bcp, int n_past_max);
+hipError_t launch_attention(const AttnCall& c, hipStream_t st);
+
+}  // namespace qk

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before launching anything.
+
+No GPU is used: every call below fails validation, which happens on the host
+before any HIP call.  Pointers are fake but aligned; should validation ever
+let one through, the call would reach the HIP runtime, so these tests are
+skipped where a device is present.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qk.h")
+
+import sparse_kv_selection_amd as qk  # noqa: E402
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, HIP = range(8)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = _declared()
+    assert "qk_qsel" in names and "qk_sparse_attn_indexed" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", qk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qk_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(qk.EXPORTED) == names
+    lib = ctypes.CDLL(qk.LIB_PATH)
+    for n in names:
+        getattr(lib, n)
+
+
+def test_version_and_strings():
+    assert qk.qk_abi_version() == 1
+    for code in range(8):
+        assert qk.qk_status_string(code)
+    assert qk.qk_status_string(99) == "unknown status"
+
+
+nogpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers; host checks only")
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+def _shape(**kw):
+    base = dict(b=1, nq=8, nkv=2, d=128, bcp=64, t_past=1000, kv_cap=1064, nq_keep=16, bsa=100,
+                scale=0.0, dtype=qk.QK_BF16)
+    base.update(kw)
+    return qk.Shape(**base).c()
+
+
+def _p(x=FAKE):
+    return ctypes.c_void_p(x) if x else None
+
+
+@nogpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(nq=7), SHAPE), (dict(nkv=0), SHAPE), (dict(b=0), SHAPE), (dict(d=96), UNSUP),
+    (dict(bcp=0), SHAPE), (dict(bcp=5000), SHAPE), (dict(kv_cap=1063), SHAPE),
+    (dict(t_past=-1), SHAPE), (dict(dtype=7), DTYPE), (dict(scale=-1.0), SHAPE),
+    (dict(nq_keep=0), SHAPE), (dict(nq_keep=65), SHAPE), (dict(nq_keep=300, bcp=512), SHAPE),
+])
+def test_qsel_rejects(kw, code):
+    lib = qk.load_library()
+    s = _shape(**kw)
+    assert lib.qk_qsel(ctypes.byref(s), _p(), _p(), None, _p(), None) == code
+
+
+@nogpu
+def test_null_and_alignment():
+    lib = qk.load_library()
+    s = _shape()
+    assert lib.qk_qsel(None, _p(), _p(), None, _p(), None) == NULL
+    assert lib.qk_qsel(ctypes.byref(s), None, _p(), None, _p(), None) == NULL
+    assert lib.qk_qsel(ctypes.byref(s), _p(FAKE + 8), _p(), None, _p(), None) == ALIGN
+    assert lib.qk_kvscore(ctypes.byref(s), _p(), _p(FAKE + 2), _p(), None) == ALIGN
+    assert lib.qk_kvscore(ctypes.byref(s), _p(), None, _p(), None) == NULL
+
+
+@nogpu
+def test_kvscore_limits():
+    lib = qk.load_library()
+    assert lib.qk_kvscore(ctypes.byref(_shape(nq_keep=65, bcp=128, kv_cap=2000)), _p(), _p(), _p(), None) == UNSUP
+    assert lib.qk_kvscore(ctypes.byref(_shape(nq_keep=33, d=256)), _p(), _p(), _p(), None) == UNSUP
+
+
+@nogpu
+def test_topk_rejects():
+    lib = qk.load_library()
+    assert lib.qk_topk(4, 100, 0, _p(), 100, _p(), 10, None, 0, None) == SHAPE
+    assert lib.qk_topk(4, 100, 10, _p(), 99, _p(), 10, None, 0, None) == SHAPE
+    assert lib.qk_topk(4, 100, 10, _p(), 100, _p(), 9, None, 0, None) == SHAPE
+    assert lib.qk_topk(-1, 100, 10, _p(), 100, _p(), 10, None, 0, None) == SHAPE
+    assert lib.qk_topk(4, 100, 10, None, 100, _p(), 10, None, 0, None) == NULL
+    assert lib.qk_topk(4, 100, 10, _p(FAKE + 2), 100, _p(), 10, None, 0, None) == ALIGN
+    # nothing to do is not an error
+    assert lib.qk_topk(0, 100, 10, None, 100, None, 10, None, 0, None) == OK
+    assert lib.qk_topk(3, 0, 10, None, 0, None, 0, None, 0, None) == OK
+
+
+@nogpu
+def test_round_select_rejects():
+    lib = qk.load_library()
+    s = _shape()
+    f = lib.qk_round_select
+    assert f(ctypes.byref(s), _p(), 0, _p(), 1, 1, _p(), 1000, _p(), None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 8, 1, _p(), 1000, _p(), None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 0, 1, _p(), 1000, _p(), None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 2, 1, _p(), 999, _p(), None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, None, 2, 1, _p(), 1000, _p(), None, None) == NULL
+
+
+@nogpu
+def test_attention_rejects():
+    lib = qk.load_library()
+    s = _shape()
+    need = lib.qk_workspace_bytes(ctypes.byref(s), qk.OPS["sparse_attn"])
+    f = lib.qk_sparse_attn_indexed
+    assert f(ctypes.byref(s), _p(), _p(), _p(), _p(), 99, None, _p(), None, _p(), 1 << 30, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), _p(), _p(), None, 100, None, _p(), None, _p(), 1 << 30, None) == NULL
+    if need:
+        assert f(ctypes.byref(s), _p(), _p(), _p(), _p(), 100, None, _p(), None, _p(), need - 1, None) == WS
+        assert f(ctypes.byref(s), _p(), _p(), _p(), _p(), 100, None, _p(), None, None, need, None) == NULL
+    g = lib.qk_sparse_attn
+    assert g(ctypes.byref(s), _p(), None, _p(), 100, None, _p(), _p(), _p(), None, _p(), 1 << 30, None) == NULL
+    assert g(ctypes.byref(s), _p(), _p(), _p(), 50, None, _p(), _p(), _p(), None, _p(), 1 << 30, None) == SHAPE
+    s32 = _shape(dtype=qk.QK_F32, d=256)
+    assert lib.qk_dense_attn(ctypes.byref(s32), _p(), _p(), _p(), _p(), None, _p(), 1 << 30, None) == UNSUP
+    assert lib.qk_gather(ctypes.byref(s), _p(), _p(), _p(), 99, None, _p(), _p(), None) == SHAPE
+
+
+def test_workspace_sizes():
+    # split-key partials: n_split * rows * (d + 1) floats, 0 when one split suffices
+    s = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192)
+    n = qk.qk_workspace_bytes(s, "sparse_attn")
+    rows = 1 * 24 * 256
+    assert n > 0 and n % (rows * 129 * 4) == 0
+    assert qk.qk_workspace_bytes(s, "qsel") == 0
+    assert qk.qk_workspace_bytes(qk.Shape(1, 4, 2, 64, 64, 1024, 1088, 32, 256, dtype=qk.QK_F32),
+                                 "sparse_attn") == 0
+    bad = qk.Shape(1, 7, 2, 128, 256, 32768, 33024, 32, 8192)
+    assert qk.qk_workspace_bytes(bad, "sparse_attn") == 0

@@ -1,0 +1,353 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle on identical seeded
+inputs, through the C ABI.
+
+Staging: a GPU stage may be fed the oracle's result of the previous stage (an
+oracle value going into the HIP path); no oracle input ever comes from the
+HIP path.  End-to-end checks compare the two pipelines run independently.
+Sizes span several tiles with ragged tails; the full-size cases compare every
+selection output and a sample of attention rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import (ATTN_TOL, BOUNDARY_TOL, LSE_TOL, SCORE_TOL, assert_set_within_boundary,
+                    assert_sorted_unique, max_abs, np64, npi)
+
+pytestmark = pytest.mark.gpu
+
+# name -> (workload, overrides, seed)
+CASES = {
+    "tiny_f32": ("tiny_f32", {}, 1001),
+    "llama_ragged": ("llama3b_32k", dict(t_past=5000, bcp=200, bsa=1300), 1002),
+    "decode_small": ("decode_64x16k", dict(b=6, t_past=3001, bsa=600), 1003),
+    "d256_small": ("long_128k_d256", dict(t_past=4100, bcp=130, nq_keep=20, bsa=900), 1005),
+    "d64_nq40": ("llama3b_32k", dict(d=64, nq=8, nkv=2, t_past=2000, bcp=100, nq_keep=40, bsa=500), 7),
+    "g1_all_keys": ("llama3b_32k", dict(nq=4, nkv=4, t_past=700, bcp=33, nq_keep=33, bsa=700), 8),
+    "f32_d128": ("tiny_f32", dict(d=128, t_past=777, bcp=45, nq_keep=9, bsa=300), 9),
+}
+ROUND_CASES = {
+    "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
+                                        top_rounds=4), 1004),
+}
+
+_cache = {}
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _case(name, table=CASES):
+    if name in _cache:
+        return _cache[name]
+    wname, over, seed = table[name]
+    spec = W.spec(wname, **over)
+    case = W.make_case(spec, seed)
+    qn, kn, vn = np64(case["q"]), np64(case["k"]), np64(case["v"])
+    off = case["round_off"].numpy() if case["round_off"] is not None else None
+    ref = oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, round_off=off,
+                          top_rounds=spec.top_rounds)
+    dev = _dev()
+    gpu = {n: case[n].to(dev) for n in ("q", "k", "v")}
+    if off is not None:
+        gpu["round_off"] = case["round_off"].to(dev)
+    _cache[name] = (spec, case, ref, gpu)
+    return _cache[name]
+
+
+def _shape(spec, qk):
+    return qk.shape_of(spec)
+
+
+# --------------------------------------------------------------------------
+# stage 1: query sub-selection and group aggregation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(CASES))
+def test_qsel(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    dev = _dev()
+    q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=torch.int32, device=dev)
+    sq = torch.empty((s.b, s.nq, s.bcp), dtype=torch.float32, device=dev)
+    qg = torch.empty((s.b, s.nkv, s.nq_keep, s.d), dtype=torch.float32, device=dev)
+    qk.qk_qsel(s, g["q"], q_idx, sq, qg)
+    torch.cuda.synchronize()
+    err = max_abs(sq, ref["sq"])
+    assert err <= SCORE_TOL and err <= 1e-5, err
+    gi = npi(q_idx)
+    G = s.group
+    agree = np.ones((s.b, s.nkv, s.nq_keep), dtype=bool)
+    for b in range(s.b):
+        for h in range(s.nq):
+            assert_set_within_boundary(gi[b, h], ref["qidx"][b, h], ref["sq"][b, h], s.nq_keep,
+                                       what=f"qidx b{b} h{h}")
+            # order: decreasing oracle SQ up to near-ties
+            assert np.all(np.diff(ref["sq"][b, h][gi[b, h]]) <= BOUNDARY_TOL)
+            agree[b, h // G] &= gi[b, h] == ref["qidx"][b, h]
+    gq = np64(qg)
+    assert np.abs(gq - ref["q_group"])[agree].max() <= 1e-5
+    # slots whose picks differ at a near-tie: the group mean of the picks made
+    qn = np64(case["q"])
+    for b, j, n in zip(*np.nonzero(~agree)):
+        rows = [qn[b, j * G + gg, gi[b, j * G + gg, n]] for gg in range(G)]
+        want = np.mean([r / np.linalg.norm(r) for r in rows], axis=0)
+        assert np.abs(gq[b, j, n] - want).max() <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# stage 2: scoring pass, fed the oracle's group queries
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(CASES))
+def test_kvscore(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    qg32 = torch.from_numpy(ref["q_group"].astype(np.float32))
+    s_agg = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    qk.qk_kvscore(s, qg32.to(_dev()), g["k"], s_agg)
+    torch.cuda.synchronize()
+    _, want = oracle.key_scores(qg32.double().numpy(), np64(case["k"]), s.t_past)
+    err = max_abs(s_agg, want)
+    assert err <= SCORE_TOL, err
+    assert err <= 5e-5, f"precision regression: {err}"   # bf16 hi/lo split: ~1e-6
+
+
+# --------------------------------------------------------------------------
+# stage 3: top-BSA on the oracle's scores (fp32) -- integer result, exact
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(CASES))
+def test_topk_on_oracle_scores(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    scores32 = ref["s_agg"].astype(np.float32)
+    rows = s.b * s.nkv
+    kk = min(s.bsa, s.t_past)
+    idx = torch.full((rows, kk), -1, dtype=torch.int32, device=_dev())
+    qk.qk_topk(rows, s.t_past, s.bsa, torch.from_numpy(scores32).to(_dev()).reshape(rows, -1),
+               s.t_past, idx, kk)
+    torch.cuda.synchronize()
+    want = oracle.select_keys(scores32.astype(np.float64), s.bsa).reshape(rows, kk)
+    assert np.array_equal(npi(idx), want)
+
+
+# --------------------------------------------------------------------------
+# stage 4: attention over the oracle's selection
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fused", [True, False], ids=["indexed", "gathered"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_attention_on_oracle_selection(gpu, name, fused):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    dev = _dev()
+    kidx = torch.from_numpy(ref["kidx"].astype(np.int32)).to(dev).contiguous()
+    n_sel = kidx.shape[-1]
+    out = torch.empty_like(g["q"])
+    lse = torch.empty((s.b, s.nq, s.bcp), dtype=torch.float32, device=dev)
+    nws = qk.qk_workspace_bytes(s, "sparse_attn")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    if fused:
+        qk.qk_sparse_attn_indexed(s, g["q"], g["k"], g["v"], kidx, n_sel, None, out, lse, ws, nws)
+    else:
+        ksel = torch.empty((s.b, s.nkv, n_sel, s.d), dtype=g["k"].dtype, device=dev)
+        vsel = torch.empty_like(ksel)
+        qk.qk_gather(s, g["k"], g["v"], kidx, n_sel, None, ksel, vsel)
+        torch.cuda.synchronize()
+        kn = np64(case["k"])
+        want_k = np.stack([[kn[b, j, ref["kidx"][b, j]] for j in range(s.nkv)] for b in range(s.b)])
+        assert np.array_equal(np64(ksel), want_k)        # a copy: bit-exact
+        qk.qk_sparse_attn(s, g["q"], ksel, vsel, n_sel, None, g["k"], g["v"], out, lse, ws, nws)
+    torch.cuda.synchronize()
+    err = max_abs(out, ref["o"])
+    assert err <= ATTN_TOL[spec.dtype], err
+    assert max_abs(lse, ref["lse"]) <= LSE_TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "llama_ragged", "decode_small", "d256_small", "d64_nq40"])
+def test_dense_attention(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    dev = _dev()
+    out = torch.empty_like(g["q"])
+    lse = torch.empty((s.b, s.nq, s.bcp), dtype=torch.float32, device=dev)
+    nws = qk.qk_workspace_bytes(s, "dense_attn")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    qk.qk_dense_attn(s, g["q"], g["k"], g["v"], out, lse, ws, nws)
+    torch.cuda.synchronize()
+    want_o, want_lse = oracle.dense_attention(np64(case["q"]), np64(case["k"]), np64(case["v"]),
+                                              s.t_past)
+    assert max_abs(out, want_o) <= ATTN_TOL[spec.dtype]
+    assert max_abs(lse, want_lse) <= LSE_TOL[spec.dtype]
+
+
+# --------------------------------------------------------------------------
+# end to end: each side runs its own pipeline
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(CASES))
+def test_pipeline_end_to_end(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    pipe = qk.Pipeline(s, device=_dev())
+    pipe(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    assert max_abs(pipe.s_agg, ref["s_agg"]) <= SCORE_TOL
+    kidx = npi(pipe.idx)
+    swaps = 0
+    for b in range(s.b):
+        for j in range(s.nkv):
+            assert_sorted_unique(kidx[b, j], s.t_past)
+            swaps += assert_set_within_boundary(kidx[b, j], ref["kidx"][b, j], ref["s_agg"][b, j],
+                                                s.n_sel, what=f"kidx b{b} j{j}")
+    if spec.dtype == "f32":
+        assert swaps == 0
+    assert max_abs(pipe.out, ref["o"]) <= ATTN_TOL[spec.dtype]
+
+
+def test_sparse_equals_dense_at_full_budget(gpu):
+    qk = gpu
+    spec, case, ref, g = _case("g1_all_keys")
+    s = _shape(spec, qk)
+    pipe = qk.Pipeline(s, device=_dev())
+    pipe(g["q"], g["k"], g["v"])
+    out = torch.empty_like(g["q"])
+    nws = qk.qk_workspace_bytes(s, "dense_attn")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=_dev())
+    qk.qk_dense_attn(s, g["q"], g["k"], g["v"], out, None, ws, nws)
+    torch.cuda.synchronize()
+    assert np.array_equal(npi(pipe.idx)[0, 0], np.arange(s.t_past))
+    assert max_abs(pipe.out, out) <= 2e-3
+
+
+# --------------------------------------------------------------------------
+# round-granular selection
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(ROUND_CASES))
+def test_round_select_and_attention(gpu, name):
+    qk = gpu
+    spec, case, ref, g = _case(name, ROUND_CASES)
+    s = _shape(spec, qk)
+    dev = _dev()
+    rows = s.b * s.nkv
+    scores32 = ref["s_agg"].astype(np.float32)
+    idx = torch.full((s.b, s.nkv, s.t_past), -1, dtype=torch.int32, device=dev)
+    sel_len = torch.empty((s.b, s.nkv), dtype=torch.int32, device=dev)
+    s_round = torch.empty((s.b, s.nkv, spec.n_rounds), dtype=torch.float32, device=dev)
+    qk.qk_round_select(s, torch.from_numpy(scores32).to(dev), spec.n_rounds, g["round_off"],
+                       spec.top_rounds, True, idx, s.t_past, sel_len, s_round)
+    torch.cuda.synchronize()
+    off = case["round_off"].numpy()
+    want_sr = oracle.round_scores(scores32.astype(np.float64), off)
+    assert np.array_equal(np64(s_round), want_sr)      # max of fp32 values: exact
+    chosen = oracle.select_rounds(want_sr, spec.top_rounds)
+    sets = oracle.round_key_sets(chosen, off)
+    gi, gl = npi(idx), npi(sel_len)
+    for b in range(s.b):
+        for j in range(s.nkv):
+            assert gl[b, j] == len(sets[b][j])
+            assert np.array_equal(gi[b, j, : gl[b, j]], sets[b][j])
+    # ragged attention over the oracle's rounds, vs the oracle
+    ld = max(len(x) for row in ref["key_sets"] for x in row)
+    kidx = np.zeros((s.b, s.nkv, ld), dtype=np.int32)
+    lens = np.zeros((s.b, s.nkv), dtype=np.int32)
+    for b in range(s.b):
+        for j in range(s.nkv):
+            ks = ref["key_sets"][b][j]
+            kidx[b, j, : len(ks)] = ks
+            lens[b, j] = len(ks)
+    s2 = qk.shape_of(spec, bsa=ld)
+    out = torch.empty_like(g["q"])
+    nws = qk.qk_workspace_bytes(s2, "sparse_attn")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    qk.qk_sparse_attn_indexed(s2, g["q"], g["k"], g["v"], torch.from_numpy(kidx).to(dev), ld,
+                              torch.from_numpy(lens).to(dev), out, None, ws, nws)
+    torch.cuda.synchronize()
+    assert max_abs(out, ref["o"]) <= ATTN_TOL[spec.dtype]
+    # and the whole round pipeline end to end
+    pipe = qk.Pipeline(s2, device=dev, n_rounds=spec.n_rounds, top_rounds=spec.top_rounds)
+    pipe(g["q"], g["k"], g["v"], g["round_off"])
+    torch.cuda.synchronize()
+    assert max_abs(pipe.out, ref["o"]) <= ATTN_TOL[spec.dtype]
+
+
+# --------------------------------------------------------------------------
+# top-k edge cases (exact against the oracle's sort on the same fp32 values)
+# --------------------------------------------------------------------------
+def _topk_check(qk, scores32, k, ld_idx=None):
+    rows, n = scores32.shape
+    kk = min(k, n)
+    ld_idx = ld_idx or kk
+    idx = torch.full((rows, ld_idx), -7, dtype=torch.int32, device=_dev())
+    qk.qk_topk(rows, n, k, torch.from_numpy(scores32).to(_dev()), n, idx, ld_idx)
+    torch.cuda.synchronize()
+    got = npi(idx)
+    want = oracle.select_keys(scores32.astype(np.float64)[None], k)[0]
+    assert np.array_equal(got[:, :kk], want)
+    assert np.all(got[:, kk:] == -7)
+
+
+def test_topk_edge_cases(gpu):
+    qk = gpu
+    rng = np.random.default_rng(3)
+    _topk_check(qk, rng.standard_normal((5, 1000)).astype(np.float32), 77)
+    _topk_check(qk, np.round(rng.standard_normal((4, 4099)), 1).astype(np.float32), 1500)  # ties
+    _topk_check(qk, np.zeros((3, 500), np.float32), 123)                                   # all equal
+    z = np.zeros((2, 64), np.float32)
+    z[:, ::2] = -0.0
+    _topk_check(qk, z, 10)                                                                 # -0 == +0
+    _topk_check(qk, rng.standard_normal((2, 100)).astype(np.float32), 100)                 # k = n
+    _topk_check(qk, rng.standard_normal((2, 100)).astype(np.float32), 150)                 # k > n
+    _topk_check(qk, rng.standard_normal((3, 1)).astype(np.float32), 1)
+    _topk_check(qk, rng.standard_normal((3, 333)).astype(np.float32), 1, ld_idx=5)
+    _topk_check(qk, rng.uniform(-1, 1, (2, 131072)).astype(np.float32), 16384)
+    # a dense cluster at the boundary (more than fits in LDS): global fallback
+    x = rng.uniform(0, 1e-6, (2, 40000)).astype(np.float32) + 0.5
+    x[:, :100] = 2.0
+    x[:, 100:200] = -2.0
+    _topk_check(qk, x, 20000)
+
+
+def test_zero_keys_and_empty_past(gpu):
+    qk = gpu
+    spec = W.spec("llama3b_32k", t_past=300, bcp=70, bsa=64)
+    case = W.make_case(spec, 21)
+    case["k"][:, :, 10:20] = 0
+    g = {n: case[n].to(_dev()) for n in ("q", "k", "v")}
+    s = qk.shape_of(spec)
+    pipe = qk.Pipeline(s, device=_dev())
+    pipe(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    assert np.all(np64(pipe.s_agg)[:, :, 10:20] == 0)
+    ref = oracle.pipeline(np64(case["q"]), np64(case["k"]), np64(case["v"]), 300, spec.nq_keep, 64)
+    assert max_abs(pipe.s_agg, ref["s_agg"]) <= SCORE_TOL
+    # no past at all: dense attention is the chunk's causal self-attention
+    s0 = qk.Shape(s.b, s.nq, s.nkv, s.d, s.bcp, 0, s.kv_cap, s.nq_keep, 1)
+    kk, vv = g["k"][:, :, 300:].contiguous(), g["v"][:, :, 300:].contiguous()
+    s0.kv_cap = kk.shape[2]
+    out = torch.empty_like(g["q"])
+    nws = qk.qk_workspace_bytes(s0, "dense_attn")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=_dev())
+    qk.qk_dense_attn(s0, g["q"], kk, vv, out, None, ws, nws)
+    torch.cuda.synchronize()
+    want, _ = oracle.dense_attention(np64(case["q"]), np64(case["k"][:, :, 300:]),
+                                     np64(case["v"][:, :, 300:]), 0)
+    assert max_abs(out, want) <= ATTN_TOL["bf16"]
+
+
+def test_deterministic(gpu):
+    qk = gpu
+    spec, case, ref, g = _case("llama_ragged")
+    s = _shape(spec, qk)
+    a = qk.Pipeline(s, device=_dev())
+    b = qk.Pipeline(s, device=_dev())
+    a(g["q"], g["k"], g["v"])
+    b(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    for n in ("q_idx", "q_group", "s_agg", "idx", "out", "lse"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
