@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--gathered", action="store_true", help="qk_gather + qk_sparse_attn instead of the fused path")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -124,6 +126,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a copy of known size: 256 MiB read + 256 MiB written per dispatch
+        n = 256 * 1024 * 1024 // 4
+        src = torch.rand(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "dispatches": 5}), flush=True)
+        return
 
     spec = W.spec(args.workload)
     rounds = spec.n_rounds > 0

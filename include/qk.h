@@ -77,10 +77,10 @@ typedef enum { QK_F32 = 0, QK_BF16 = 1 } qk_dtype;
 /* [host] Problem description shared by the calls. */
 typedef struct {
   int32_t b;        /* sequences in the batch, >= 1                              */
-  int32_t nq;       /* query heads, a multiple of nkv                            */
+  int32_t nq;       /* query heads, a multiple of nkv, at most 64 * nkv          */
   int32_t nkv;      /* KV heads, >= 1                                            */
   int32_t d;        /* head dim: 64, 128 or 256                                  */
-  int32_t bcp;      /* chunk queries, 1 .. 8192 (1 = decode)                     */
+  int32_t bcp;      /* chunk queries, 1 .. 4096 (1 = decode)                     */
   int32_t t_past;   /* T, past positions scored, >= 0 (>= 1 for selection)        */
   int32_t kv_cap;   /* rows per (sequence, KV head) in k and v, >= t_past + bcp  */
   int32_t nq_keep;  /* NQ, kept queries per head, 1 .. min(bcp, 256)             */

@@ -22,6 +22,7 @@ qk_status check_shape(const qk_shape* s) {
   if (s->dtype != QK_F32 && s->dtype != QK_BF16) return QK_ERR_DTYPE;
   if (s->b < 1 || s->nkv < 1 || s->nq < s->nkv || s->nq % s->nkv != 0) return QK_ERR_SHAPE;
   if (s->d != 64 && s->d != 128 && s->d != 256) return QK_ERR_UNSUPPORTED;
+  if (s->nq / s->nkv > 64) return QK_ERR_UNSUPPORTED;
   if (s->bcp < 1 || s->bcp > 4096) return QK_ERR_SHAPE;
   if (s->t_past < 0) return QK_ERR_SHAPE;
   if (static_cast<int64_t>(s->kv_cap) < static_cast<int64_t>(s->t_past) + s->bcp) return QK_ERR_SHAPE;

@@ -26,6 +26,8 @@
 // fp32 kernel: one thread per query row, fp32 throughout (small workloads).
 #include <math.h>
 
+#include <type_traits>
+
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -55,8 +57,8 @@ struct AttnParams {
 
 constexpr int kKeyTile = 64;
 
-template <int D, int NB, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) {
+template <int D, int NB, int WAVES, int OCC>
+__global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p) {
   constexpr int NT = 64 * WAVES;
   constexpr int ROWS = WAVES * NB * 32;
   constexpr int KSTR = D + 8;          // sK row stride, elements
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
   constexpr int VUNITS = 16 * CH;      // units of 4 rows x 16 bytes
   constexpr int KPER = (KUNITS + NT - 1) / NT;
   constexpr int VPER = (VUNITS + NT - 1) / NT;
-  constexpr bool kPrefetch = WAVES > 1;
+  constexpr bool kPrefetch = true;
   __shared__ __attribute__((aligned(16))) uint16_t sK[kKeyTile * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sVT[D * VSTR];
 
@@ -84,7 +86,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
 
   // past rows available: the index list length, or the rows of the past buffer
   const int past_cap = p.idx ? p.ld_idx : static_cast<int>(p.past_bj_rows);
-  const int n_past = min(p.sel_len ? p.sel_len[bj] : p.n_past, past_cap);
+  // wave-uniform (readfirstlane): tile classification below branches on it
+  const int n_past =
+      __builtin_amdgcn_readfirstlane(min(p.sel_len ? p.sel_len[bj] : p.n_past, past_cap));
   const int past_tiles = (n_past + kKeyTile - 1) / kKeyTile;
   // splits are balanced over this (b, KV head)'s own selection length
   const int split_tiles = (past_tiles + p.n_split - 1) / p.n_split;
@@ -102,6 +106,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
   const uint16_t* ck = p.k + (static_cast<size_t>(bj) * p.kv_cap + p.t_past) * D;
   const uint16_t* cv = p.v + (static_cast<size_t>(bj) * p.kv_cap + p.t_past) * D;
   const int32_t* idx = p.idx ? p.idx + static_cast<size_t>(bj) * p.ld_idx : nullptr;
+  const int row_hi = static_cast<int>(p.past_bj_rows) - 1;
+
+  // Element offset of tile key r.  Keys past the end of the range are clamped
+  // onto a valid row: they are masked to -inf, so their weight is exactly 0.
+  auto key_off = [&](int t, int r) -> int {
+    if (t < npt) {
+      const int kk = min((pt0 + t) * kKeyTile + r, n_past - 1);
+      const int row = idx ? min(max(idx[kk], 0), row_hi) : kk;
+      return row * D;
+    }
+    return min((t - npt) * kKeyTile + r, bcp - 1) * D;
+  };
 
   // query fragments: lane (col, half) holds row col of block nb, d slots 16s + 8half + [0,8)
   bf16x8 qf[NB][D / 16];
@@ -118,6 +134,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
       qf[nb][s] = valid ? as_bf16x8(ld16(qp + 16 * s + 8 * half)) : bf16x8{};
   }
 
+  // a wave whose rows are all padding only helps with the tile loads
+  const bool wave_active = row0 + wave * NB * 32 < M;
+
   f32x16 acc[NB][D / 32];
   float m_run[NB], l_run[NB];
 #pragma unroll
@@ -128,32 +147,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
     for (int db = 0; db < D / 32; ++db) acc[nb][db] = f32x16{};
   }
 
+  // Tile loads.  Offsets for tile t+1 are computed (index loads) while tile t
+  // is in flight, so index and data loads never wait on each other.
+  int koff[KPER], voff[VPER][4];
   u32x4 kreg[KPER];
   u32x4 vreg[VPER][4];
-
-  // row pointer of tile key r (or nullptr: outside the key range)
-  auto key_src = [&](int t, int r, bool is_v) -> const uint16_t* {
-    if (t < npt) {
-      const int kk = (pt0 + t) * kKeyTile + r;
-      if (kk >= n_past) return nullptr;
-      // index entries are clamped into the buffer (valid lists are unaffected)
-      const int row = idx ? min(max(idx[kk], 0), static_cast<int>(p.past_bj_rows) - 1) : kk;
-      return (is_v ? pv : pk) + static_cast<size_t>(row) * D;
-    }
-    const int uu = (t - npt) * kKeyTile + r;
-    if (uu >= bcp) return nullptr;
-    return (is_v ? cv : ck) + static_cast<size_t>(uu) * D;
-  };
-
-  auto fetch = [&](int t) {
+  auto offsets = [&](int t) {
 #pragma unroll
     for (int pp = 0; pp < KPER; ++pp) {
       const int u = tid + pp * NT;
-      if (KUNITS % NT == 0 || u < KUNITS) {
-        const int r = u / CH, c = u - (u / CH) * CH;
-        const uint16_t* src = key_src(t, r, false);
-        kreg[pp] = src ? ld16(src + 8 * c) : u32x4{};
-      }
+      if (KUNITS % NT == 0 || u < KUNITS) koff[pp] = key_off(t, u / CH) + 8 * (u % CH);
     }
 #pragma unroll
     for (int pp = 0; pp < VPER; ++pp) {
@@ -163,10 +166,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
         const int q4 = sg & 3;
         const int kb4 = (sg >> 2) * 16 + (q4 & 1) * 8 + (q4 >> 1) * 4;
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const uint16_t* src = key_src(t, kb4 + e4, true);
-          vreg[pp][e4] = src ? ld16(src + 8 * c) : u32x4{};
-        }
+        for (int e4 = 0; e4 < 4; ++e4) voff[pp][e4] = key_off(t, kb4 + e4) + 8 * c;
+      }
+    }
+  };
+  auto fetch = [&](int t) {
+    const uint16_t* kbase = t < npt ? pk : ck;
+    const uint16_t* vbase = t < npt ? pv : cv;
+#pragma unroll
+    for (int pp = 0; pp < KPER; ++pp) {
+      const int u = tid + pp * NT;
+      if (KUNITS % NT == 0 || u < KUNITS) kreg[pp] = ld16(kbase + koff[pp]);
+    }
+#pragma unroll
+    for (int pp = 0; pp < VPER; ++pp) {
+      const int u = tid + pp * NT;
+      if (VUNITS % NT == 0 || u < VUNITS) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) vreg[pp][e4] = ld16(vbase + voff[pp][e4]);
       }
     }
   };
@@ -205,12 +222,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
     }
   };
 
-  if (n_tiles > 0) fetch(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  const float c2 = p.scale_log2;
+  if (n_tiles > 0) {
+    offsets(0);
+    fetch(0);
+    if (n_tiles > 1) offsets(1);
+  }
+  auto tile = [&](int t, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     __syncthreads();
     store();
     __syncthreads();
-    if (kPrefetch && t + 1 < n_tiles) fetch(t + 1);
+    if (kPrefetch && t + 1 < n_tiles) {
+      fetch(t + 1);
+      if (t + 2 < n_tiles) offsets(t + 2);
+    }
+    if (!wave_active) return;
 
     // S^T = K Q^T for 64 keys x (NB * 32) queries
     f32x16 S[2][NB];
@@ -229,50 +256,50 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
       }
     }
 
-    // mask, scale, online softmax (base 2); P^T fragments in bf16
+    // mask (boundary and chunk tiles only), online softmax in base 2
     const bool is_chunk = t >= npt;
     const int kbase = is_chunk ? (t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
-    const int klimit = is_chunk ? bcp : n_past;
     bf16x8 P[NB][4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float x[2][16];
-      float mx = -INFINITY;
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (kMasked) {
+          const int klimit = is_chunk ? min(bcp, iq[nb] + 1) : n_past;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + kb * 32 + acc_row(r, half);
-          bool ok = key < klimit;
-          if (is_chunk) ok = ok && key <= iq[nb];
-          x[kb][r] = ok ? S[kb][nb][r] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, x[kb][r]);
+            for (int r = 0; r < 16; ++r)
+              if (kbase + kb * 32 + acc_row(r, half) >= klimit) S[kb][nb][r] = -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[nb] - m_use);
-      m_run[nb] = m_new;
-      float ps = 0.f;
+        float mx = S[0][nb][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          x[kb][r] = exp2f(x[kb][r] - m_use);
-          ps += x[kb][r];
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][nb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+        const float m_new = fmaxf(m_run[nb], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
+        m_run[nb] = m_new;
+        float ps = 0.f;
+#pragma unroll
+        for (int g16 = 0; g16 < 4; ++g16) {
+          const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e], c2, -m_use));
+            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e + 1], c2, -m_use));
+            ps += x0 + x1;
+            w[e] = pack_bf16x2(x0, x1);
+          }
+          P[nb][g16] = as_bf16x8(w);
         }
-      l_run[nb] = l_run[nb] * alpha + ps;
+        l_run[nb] = l_run[nb] * alpha + ps;
+        if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
-#pragma unroll
-      for (int g16 = 0; g16 < 4; ++g16) {
-        const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[kb][r0 + 2 * e], x[kb][r0 + 2 * e + 1]);
-        P[nb][g16] = as_bf16x8(w);
+          for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
+        }
       }
-    }
 
     // O^T += V^T P^T
 #pragma unroll
@@ -285,8 +312,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
         for (int nb = 0; nb < NB; ++nb) acc[nb][db] = mfma32(a, P[nb][g16], acc[nb][db]);
       }
     }
-    if (!kPrefetch && t + 1 < n_tiles) fetch(t + 1);
-  }
+  };
+  // leading tiles wholly inside the past range need no mask
+  const int n_full = min(max(n_past / kKeyTile - pt0, 0), npt);
+  for (int t = 0; t < n_full; ++t) tile(t, std::false_type{});
+  for (int t = n_full; t < n_tiles; ++t) tile(t, std::true_type{});
 
   // epilogue: lane (col, half) holds query col, d rows db*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
@@ -328,31 +358,49 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(AttnParams p) 
   }
 }
 
-// Merge key-split partials: O = sum_s w_s O_s / sum_s w_s, w_s = 2^(lse_s - max).
-template <typename OutT>
+// Merge key-split partials, one wave per output row:
+//   O = sum_s w_s O_s / sum_s w_s,  w_s = 2^(lse_s - max_s lse_s)
+// Lane s < n_split (<= 64) holds split s's log-sum-exp; every lane then loads
+// its d-slots of all splits at once.
+template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
-                                                           OutT* __restrict__ out,
+                                                           uint16_t* __restrict__ out,
                                                            float* __restrict__ lse, int n_split,
-                                                           long long rows, int d) {
-  const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long long row = gid / d;
-  const int c = static_cast<int>(gid - row * d);
+                                                           long long rows) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[s * rows + row]);
-  float wsum = 0.f, a = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float w = exp2f(part_lse[s * rows + row] - mx);
-      wsum += w;
-      a += w * part_o[(s * rows + row) * d + c];
+  const float ls = lane < n_split ? part_lse[lane * rows + row] : -INFINITY;
+  const float mx = wave_max(ls);
+  const float w = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+  const float wsum = wave_sum(w);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  constexpr int kBatch = 16;
+  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+    float x[kBatch][PER];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sidx = min(s0 + u, n_split - 1);
+      const float* src = part_o + (sidx * rows + row) * D + lane;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) x[u][e] = src[64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float wu = s0 + u < n_split ? __shfl(w, s0 + u) : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += wu * x[u][e];
     }
   }
-  const float o = wsum > 0.f ? a / wsum : 0.f;
-  if constexpr (sizeof(OutT) == 2) out[row * d + c] = f32_to_bf16(o);
-  else out[row * d + c] = o;
-  if (lse && c == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* op = out + row * D + lane;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[64 * e] = f32_to_bf16(acc[e] * inv);
+  if (lse && lane == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: one thread per packed query row, natural-base online softmax.
@@ -408,30 +456,27 @@ Plan make_plan(int b, int nq, int nkv, int d, int bcp, int n_past_max) {
   Plan pl{};
   const int G = nq / nkv;
   const int M = G * bcp;
-  if (M <= 32) {
-    pl.waves = 1;
-    pl.nb = 1;
-  } else {
-    pl.waves = 4;
-    pl.nb = 1;
-  }
+  pl.waves = 4;
+  pl.nb = 1;
   pl.rows = pl.waves * pl.nb * 32;
   pl.n_qtiles = (M + pl.rows - 1) / pl.rows;
   const int past_tiles = (n_past_max + kKeyTile - 1) / kKeyTile;
   const long long base = static_cast<long long>(pl.n_qtiles) * b * nkv;
-  const long long target = pl.waves == 1 ? 2048 : 512;
-  long long ns = (target + base - 1) / base;
+  // key splits fill the resident slots (256 CUs x workgroups per CU) without
+  // spilling into a second, mostly idle round; at least 4 key tiles per split
+  const long long slots = 256LL * (d == 256 ? 1 : 2);
+  long long ns = slots / base;
   const long long max_split = past_tiles / 4 > 1 ? past_tiles / 4 : 1;
   if (ns > max_split) ns = max_split;
+  if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
   pl.n_split = static_cast<int>(ns);
-  (void)d;
   return pl;
 }
 
-template <int D, int NB, int WAVES>
+template <int D, int NB, int WAVES, int OCC>
 hipError_t run_bf16(const AttnParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NB, WAVES>), dim3(grid), dim3(64 * WAVES), 0, st, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NB, WAVES, OCC>), dim3(grid), dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 
@@ -493,22 +538,21 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   }
   const int grid = pl.n_qtiles * c.b * c.nkv * pl.n_split;
   hipError_t e;
-  if (pl.waves == 4) {
-    if (c.d == 128) e = run_bf16<128, 1, 4>(p, grid, st);
-    else if (c.d == 64) e = run_bf16<64, 1, 4>(p, grid, st);
-    else if (c.d == 256) e = run_bf16<256, 1, 4>(p, grid, st);
-    else return hipErrorInvalidValue;
-  } else {
-    if (c.d == 128) e = run_bf16<128, 1, 1>(p, grid, st);
-    else if (c.d == 64) e = run_bf16<64, 1, 1>(p, grid, st);
-    else if (c.d == 256) e = run_bf16<256, 1, 1>(p, grid, st);
-    else return hipErrorInvalidValue;
-  }
+  if (c.d == 128) e = run_bf16<128, 1, 4, 2>(p, grid, st);
+  else if (c.d == 64) e = run_bf16<64, 1, 4, 2>(p, grid, st);
+  else if (c.d == 256) e = run_bf16<256, 1, 4, 1>(p, grid, st);
+  else return hipErrorInvalidValue;
   if (e != hipSuccess || pl.n_split == 1) return e;
-  const long long total = static_cast<long long>(rows) * c.d;
-  hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, dim3(static_cast<unsigned>((total + 255) / 256)),
-                     dim3(256), 0, st, p.part_o, p.part_lse, static_cast<uint16_t*>(c.out), c.lse,
-                     pl.n_split, static_cast<long long>(rows), c.d);
+  const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4)), cblock(256);
+  if (c.d == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+                       static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
+  else if (c.d == 64)
+    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+                       static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+                       static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
   return hipGetLastError();
 }
 

@@ -7,10 +7,11 @@
 // Rounds: Round Attention press release (Moore Threads), sections 01-02: the
 // KV cache is cut at dialogue-round boundaries and the most relevant rounds are
 // kept as whole blocks.  A round's score is the max of the aggregated key score
-// over its positions; the latest round is always kept.  One workgroup per
-// (sequence, KV head): wave-level max per round, a rank count for the top
-// rounds (ties: lower round id), then the chosen rounds' positions are written
-// out in ascending order.
+// over its positions; the latest round is always kept.  One workgroup of 1024
+// threads per (sequence, KV head): each thread scans runs of consecutive scores
+// and merges per-round maxima with integer atomics on order-preserving keys in
+// LDS; a rank count picks the top rounds (ties: lower round id); a block prefix
+// sum places them, and their positions are written out in ascending order.
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -37,65 +38,129 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
   st16(v_sel + dst, ld16(v + src));
 }
 
-constexpr int kRoundThreads = 256;
+constexpr int kRoundThreads = 1024;
+constexpr int kRoundWaves = kRoundThreads / 64;
+constexpr int kRun = 16;  // consecutive scores per thread per pass
+
+// Order-preserving float <-> uint32 maps (for integer atomic max in LDS).
+__device__ __forceinline__ uint32_t okey(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ofloat(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Block-wide exclusive prefix sum over kRoundThreads threads.
+__device__ int round_excl_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kRoundWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kRoundWaves; o <<= 1) {
+      const int y = __shfl_up(w, o);
+      if (lane >= o) w += y;
+    }
+    if (lane < kRoundWaves) wsum[lane] = w;
+  }
+  __syncthreads();
+  const int off = wave > 0 ? wsum[wave - 1] : 0;
+  *total = wsum[kRoundWaves - 1];
+  __syncthreads();
+  return off + x - v;
+}
 
 __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
     const float* __restrict__ s_agg, int t_past, int n_rounds, const int32_t* __restrict__ off,
     int top_r, int keep_latest, int32_t* __restrict__ idx, int ld_idx,
     int32_t* __restrict__ sel_len, float* __restrict__ s_round_out) {
-  extern __shared__ float rs[];                              // [n_rounds] round scores
-  int* base = reinterpret_cast<int*>(rs + n_rounds);         // [n_rounds] output offsets, -1 = not chosen
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ int sm[];
+  int* so = sm;                                           // [n_rounds + 1] clamped offsets
+  uint32_t* rkey = reinterpret_cast<uint32_t*>(so + n_rounds + 1);  // [n_rounds] max keys
+  int* base = reinterpret_cast<int*>(rkey + n_rounds);    // [n_rounds] output offset, -1 = dropped
+  __shared__ int wsum[kRoundWaves];
+  const int tid = threadIdx.x;
   const int bj = blockIdx.x;
   const float* row = s_agg + static_cast<size_t>(bj) * t_past;
 
-  // round bounds are clamped into [0, t_past] (valid offsets are unaffected)
-  auto lo = [&](int r) { return min(max(off[r], 0), t_past); };
-  for (int r = wave; r < n_rounds; r += kRoundThreads / 64) {
-    float m = -INFINITY;
-    for (int t = lo(r) + lane; t < lo(r + 1); t += 64) m = fmaxf(m, row[t]);
-    m = wave_max(m);
-    if (lane == 0) {
-      rs[r] = m;
-      if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = m;
+  // round bounds, clamped into [0, t_past] (valid offsets are unaffected)
+  for (int r = tid; r <= n_rounds; r += kRoundThreads) so[r] = min(max(off[r], 0), t_past);
+  for (int r = tid; r < n_rounds; r += kRoundThreads) rkey[r] = 0u;
+  __syncthreads();
+
+  // 1. round maxima: each thread scans runs of kRun consecutive scores (all
+  //    loads of a run in flight), tracking the round it is in
+  for (int i0 = tid * kRun; i0 < t_past; i0 += kRoundThreads * kRun) {
+    float x[kRun];
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) x[e] = i0 + e < t_past ? row[i0 + e] : -INFINITY;
+    int lo = 0, hi = n_rounds - 1;  // round holding i0: largest r with so[r] <= i0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (so[mid] <= i0) lo = mid; else hi = mid - 1;
     }
+    int r = lo;
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) {
+      if (i0 + e >= t_past) break;
+      while (r + 1 < n_rounds && i0 + e >= so[r + 1]) {
+        if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
+        m = -INFINITY;
+        ++r;
+      }
+      m = fmaxf(m, x[e]);
+    }
+    if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
   }
   __syncthreads();
 
+  // 2. chosen rounds by rank (ties: lower round id); the latest is always kept
   const int n_cand = keep_latest ? n_rounds - 1 : n_rounds;
   for (int r = tid; r < n_rounds; r += kRoundThreads) {
-    bool chosen;
-    if (r >= n_cand) {
-      chosen = true;  // the latest round
-    } else {
-      const float s = rs[r];
+    const float sr = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
+    if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = sr;
+    bool chosen = true;
+    if (r < n_cand) {
       int rank = 0;
       for (int r2 = 0; r2 < n_cand; ++r2) {
-        const float s2 = rs[r2];
-        rank += (s2 > s) | ((s2 == s) & (r2 < r));
+        const float s2 = rkey[r2] ? ofloat(rkey[r2]) : -INFINITY;
+        rank += (s2 > sr) | ((s2 == sr) & (r2 < r));
       }
       chosen = rank < top_r;
     }
     base[r] = chosen ? 1 : -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int r = 0; r < n_rounds; ++r) {
-      if (base[r] > 0) {
-        base[r] = acc;
-        acc += max(lo(r + 1) - lo(r), 0);
-      }
-    }
-    sel_len[bj] = min(acc, ld_idx);
+
+  // 3. output offsets of the chosen rounds, in round order
+  int running = 0;
+  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads) {
+    const int r = r0 + tid;
+    const int len = (r < n_rounds && base[r] > 0) ? so[r + 1] - so[r] : 0;
+    int tot;
+    const int ex = round_excl_scan(len, wsum, &tot);
+    if (r < n_rounds) base[r] = base[r] > 0 ? running + ex : -1;
+    running += tot;
   }
+  if (tid == 0) sel_len[bj] = min(running, ld_idx);
   __syncthreads();
+
+  // 4. positions of the chosen rounds, ascending
   int32_t* out = idx + static_cast<size_t>(bj) * ld_idx;
-  for (int r = wave; r < n_rounds; r += kRoundThreads / 64) {
+  for (int r = 0; r < n_rounds; ++r) {
     const int b0 = base[r];
     if (b0 < 0) continue;
-    for (int t = lo(r) + lane; t < lo(r + 1); t += 64) {
-      const int o = b0 + (t - lo(r));
+    for (int t = so[r] + tid; t < so[r + 1]; t += kRoundThreads) {
+      const int o = b0 + (t - so[r]);
       if (o < ld_idx) out[o] = t;
     }
   }
@@ -121,7 +186,7 @@ hipError_t launch_gather(int esz, const void* k, const void* v, const int32_t* i
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,
                                const int32_t* off, int top_r, int keep_latest, int32_t* idx,
                                int ld_idx, int32_t* sel_len, float* s_round, hipStream_t st) {
-  const size_t shm = static_cast<size_t>(n_rounds) * (sizeof(float) + sizeof(int));
+  const size_t shm = sizeof(int) * (3 * static_cast<size_t>(n_rounds) + 1);
   hipLaunchKernelGGL(round_select_kernel, dim3(bnkv), dim3(kRoundThreads), shm, st, s_agg, t_past,
                      n_rounds, off, top_r, keep_latest, idx, ld_idx, sel_len, s_round);
   return hipGetLastError();

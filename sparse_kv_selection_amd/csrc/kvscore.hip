@@ -6,18 +6,21 @@
 // |k| > 0 (a zero key scores 0 on both readings).
 //
 // The pass is bound by HBM: every past key (d bf16) is read once and 4 bytes
-// are written per key.  Layout of the bf16 kernel (d = 64/128/256):
-//   * a workgroup of 4 waves streams tiles of 128 keys of one (b, KV head);
-//     each tile is fetched with coalesced 16-byte loads into registers one tile
-//     ahead (prefetch), then written to LDS with a 16-byte row pad;
-//   * wave w takes keys [32w, 32w + 32) of the tile and multiplies them with the
-//     group queries on the matrix cores (32x32x16 bf16, queries as rows, keys
-//     as columns), so the max over queries is a max over one lane's 16
-//     accumulators plus one exchange with the other lane half;
+// are written per key.  bf16 kernel (d = 64/128/256):
+//   * every wave streams its own run of 32-key blocks -- no LDS, no barriers.
+//     Lane (c, h) loads key c's d-slots [16s + 8h, 16s + 8h + 8) as one
+//     16-byte load per step s, which is exactly the matrix-core operand
+//     layout (keys as the 32 columns of a 32x32x16 bf16 tile); every load
+//     instruction covers 32 B of each of 32 rows and four consecutive steps
+//     consume whole 128-byte lines;
+//   * blocks are kept STAGES - 1 ahead in registers (unrolled ring), so each
+//     wave has that many 8 KiB blocks (d = 128) in flight;
+//   * queries are the 32 rows of the tile, so the max over queries is a max
+//     over one lane's 16 accumulators plus one exchange with the other half;
 //   * the fp32 group queries are split into bf16 high and low parts and both
 //     are multiplied (error about 2^-16 relative instead of 2^-8); the matrix
 //     cores stay far below their roofline either way;
-//   * |k|^2 is summed in fp32 from the same fragments.
+//   * |k|^2 is summed in fp32 from the same registers.
 // Query rows beyond NQ in the last 32-row block repeat query 0, which leaves
 // the max unchanged.
 #include "qk_device.h"
@@ -26,33 +29,39 @@
 namespace qk {
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreTile = 128;  // keys per tile (32 per wave)
+constexpr int kScoreWaves = 4;     // independent waves per workgroup
+constexpr int kBlock = 32;         // keys per block (one tile column set)
 
-template <int D, int NQB>
-__global__ __launch_bounds__(kScoreThreads, 2) void kvscore_bf16_kernel(
+template <int D, int NQB, int STAGES>
+__global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
     const float* __restrict__ q_group, const uint16_t* __restrict__ k, float* __restrict__ s_agg,
-    int t_past, int kv_cap, int nq_keep, int tiles_per_bj, int tiles_per_wg) {
-  constexpr int kRowElems = D + 8;                 // 16-byte pad per row
-  constexpr int kChunks = D / 8;                   // 16-byte chunks per row
-  constexpr int kUnits = kScoreTile * kChunks;     // 16-byte units per tile
-  constexpr int kPer = kUnits / kScoreThreads;     // units per thread
-  static_assert(kUnits % kScoreThreads == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kScoreTile * kRowElems];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int bnkv, int t_past, int kv_cap, int nq_keep, int blocks_per_bj, int blocks_per_wave) {
+  constexpr int NS = D / 16;  // k-steps per key
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int wgs_per_bj = (tiles_per_bj + tiles_per_wg - 1) / tiles_per_wg;
-  const int bj = blockIdx.x / wgs_per_bj;
-  const int tile0 = (blockIdx.x % wgs_per_bj) * tiles_per_wg;
-  const int tile1 = min(tile0 + tiles_per_wg, tiles_per_bj);
-  if (tile0 >= tile1) return;
+  const int waves_per_bj = (blocks_per_bj + blocks_per_wave - 1) / blocks_per_wave;
+  const int gw = blockIdx.x * kScoreWaves + wave;
+  const int bj = gw / waves_per_bj;
+  const int blk0 = (gw % waves_per_bj) * blocks_per_wave;
+  const int blk1 = min(blk0 + blocks_per_wave, blocks_per_bj);
+  if (bj >= bnkv || blk0 >= blk1) return;
 
-  const uint16_t* kb = k + static_cast<size_t>(bj) * kv_cap * D;
+  const uint16_t* kb = k + static_cast<size_t>(bj) * kv_cap * D + 8 * half;
   float* out = s_agg + static_cast<size_t>(bj) * t_past;
 
-  // group-query fragments, hi and lo bf16 parts
-  bf16x8 qhi[NQB][D / 16], qlo[NQB][D / 16];
+  u32x4 buf[STAGES][NS];
+  auto load_block = [&](int blk, u32x4* dst) {
+    const int row = min(blk * kBlock + col, kv_cap - 1);
+    const uint16_t* src = kb + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) dst[s] = ld16(src + 16 * s);
+  };
+  // first blocks in flight before the query fragments are built
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (blk0 + i < blk1) load_block(blk0 + i, buf[i]);
+
+  bf16x8 qhi[NQB][NS], qlo[NQB][NS];
   {
     const float* qg = q_group + static_cast<size_t>(bj) * nq_keep * D;
 #pragma unroll
@@ -60,18 +69,17 @@ __global__ __launch_bounds__(kScoreThreads, 2) void kvscore_bf16_kernel(
       int row = mb * 32 + col;
       if (row >= nq_keep) row = 0;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
+      for (int s = 0; s < NS; ++s) {
         const float* src = qg + static_cast<size_t>(row) * D + 16 * s + 8 * half;
-        f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-        f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-        float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         u32x4 hi, lo;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint16_t h0 = f32_to_bf16(x[2 * p]), h1 = f32_to_bf16(x[2 * p + 1]);
-          const float r0 = x[2 * p] - bf16_to_f32(h0), r1 = x[2 * p + 1] - bf16_to_f32(h1);
           hi[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-          lo[p] = pack_bf16x2(r0, r1);
+          lo[p] = pack_bf16x2(x[2 * p] - bf16_to_f32(h0), x[2 * p + 1] - bf16_to_f32(h1));
         }
         qhi[mb][s] = as_bf16x8(hi);
         qlo[mb][s] = as_bf16x8(lo);
@@ -79,44 +87,19 @@ __global__ __launch_bounds__(kScoreThreads, 2) void kvscore_bf16_kernel(
     }
   }
 
-  u32x4 pre[kPer];
-  auto fetch = [&](int tile) {
-    const int key0 = tile * kScoreTile;
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int u = tid + p * kScoreThreads;
-      const int r = u / kChunks, c = u - r * kChunks;
-      const int row = min(key0 + r, kv_cap - 1);
-      pre[p] = ld16(kb + static_cast<size_t>(row) * D + 8 * c);
-    }
-  };
-
-  fetch(tile0);
-  for (int tile = tile0; tile < tile1; ++tile) {
-    __syncthreads();  // previous tile's LDS reads are done
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int u = tid + p * kScoreThreads;
-      const int r = u / kChunks, c = u - r * kChunks;
-      st16(sk + r * kRowElems + 8 * c, pre[p]);
-    }
-    __syncthreads();
-    if (tile + 1 < tile1) fetch(tile + 1);
-
+  auto score_block = [&](int blk, const u32x4* w) {
     f32x16 acc[NQB];
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) acc[mb] = f32x16{};
     float n2 = 0.f;
-    const uint16_t* krow = sk + (wave * 32 + col) * kRowElems + 8 * half;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(krow + 16 * s);
+    for (int s = 0; s < NS; ++s) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float a = bf16lo(w[p]), bb = bf16hi(w[p]);
+        const float a = bf16lo(w[s][p]), bb = bf16hi(w[s][p]);
         n2 += a * a + bb * bb;
       }
-      const bf16x8 kf = as_bf16x8(w);
+      const bf16x8 kf = as_bf16x8(w[s]);
 #pragma unroll
       for (int mb = 0; mb < NQB; ++mb) {
         acc[mb] = mfma32(qhi[mb][s], kf, acc[mb]);
@@ -130,8 +113,20 @@ __global__ __launch_bounds__(kScoreThreads, 2) void kvscore_bf16_kernel(
       for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[mb][r]);
     m = fmaxf(m, __shfl_xor(m, 32));
     n2 += __shfl_xor(n2, 32);
-    const int key = tile * kScoreTile + wave * 32 + col;
+    const int key = blk * kBlock + col;
     if (half == 0 && key < t_past) out[key] = m / fmaxf(sqrtf(n2), kEps);
+  };
+
+  // unrolled ring: block blk lives in buf[(blk - blk0) % STAGES]
+  for (int base = blk0; base < blk1; base += STAGES) {
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i) {
+      const int blk = base + i;
+      if (blk >= blk1) break;
+      const int nxt = blk + STAGES - 1;
+      if (nxt < blk1) load_block(nxt, buf[(i + STAGES - 1) % STAGES]);
+      score_block(blk, buf[i]);
+    }
   }
 }
 
@@ -162,13 +157,17 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(const float* __restric
 template <int D, int NQB>
 void launch_bf16(const float* qg, const uint16_t* k, float* s, int bnkv, int t_past, int kv_cap,
                  int nq_keep, hipStream_t st) {
-  const int tiles_per_bj = (t_past + kScoreTile - 1) / kScoreTile;
-  const long long total = static_cast<long long>(tiles_per_bj) * bnkv;
-  int tpw = static_cast<int>(total / 2048);
-  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
-  const int wgs_per_bj = (tiles_per_bj + tpw - 1) / tpw;
-  hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB>), dim3(wgs_per_bj * bnkv), dim3(kScoreThreads),
-                     0, st, qg, k, s, t_past, kv_cap, nq_keep, tiles_per_bj, tpw);
+  constexpr int STAGES = 4;
+  const int blocks_per_bj = (t_past + kBlock - 1) / kBlock;
+  // about one resident wave per SIMD, each streaming a run of blocks
+  const long long total = static_cast<long long>(blocks_per_bj) * bnkv;
+  long long bpw = (total + 1023) / 1024;
+  if (bpw < 2) bpw = 2;
+  if (bpw > blocks_per_bj) bpw = blocks_per_bj;
+  const long long waves = ((blocks_per_bj + bpw - 1) / bpw) * static_cast<long long>(bnkv);
+  const int wgs = static_cast<int>((waves + kScoreWaves - 1) / kScoreWaves);
+  hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES>), dim3(wgs), dim3(64 * kScoreWaves), 0,
+                     st, qg, k, s, bnkv, t_past, kv_cap, nq_keep, blocks_per_bj, static_cast<int>(bpw));
 }
 
 }  // namespace

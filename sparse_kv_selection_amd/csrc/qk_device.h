@@ -28,8 +28,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   __bf16 h = static_cast<__bf16>(x);
   return __builtin_bit_cast(uint16_t, h);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32), round to nearest even
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <typename T> struct Elem;

@@ -4,18 +4,20 @@
 // aggregated score per KV head.  Ties go to the lower position and -0.0
 // equals +0.0, so the selected set is unique.
 //
-// One workgroup of 1024 threads per row; the row stays in L2 between passes:
+// One workgroup of 1024 threads per row; every thread owns contiguous runs of
+// the row (so the index-order compaction needs one prefix sum per run):
 //   1. min / max of the row;
-//   2. histogram over 2048 equal-width value bins between min and max (the
-//      binning is monotone in the value, so every bin above the one that holds
-//      the k-th largest value is selected whole);
-//   3. the elements of that boundary bin are collected in LDS and an exact
-//      8-bit radix select over their order-preserving 32-bit keys finds the
-//      threshold key and how many elements equal to it are still needed (if
-//      the bin holds more than the LDS capacity, the same radix select runs
-//      over the row in global memory instead);
-//   4. compaction in index order with block-wide prefix sums: every element
-//      above the threshold, plus the first `need` elements equal to it.
+//   2. histogram over 2048 equal-width value bins between min and max -- the
+//      binning is monotone in the value, so every bin above the one holding
+//      the k-th largest value is selected whole;
+//   3. an exact 8-bit radix select over the order-preserving 32-bit keys of
+//      that boundary bin's elements gives the threshold key and how many
+//      elements equal to it are still needed;
+//   4. compaction in index order: every element above the threshold, plus the
+//      first `need` elements equal to it.
+// Rows of up to 16K scores are read once into registers; longer rows are
+// streamed in runs of 16 per thread with all loads of a run in flight (after
+// the first pass the row is served from L2).
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -25,7 +27,7 @@ namespace {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
-constexpr int kCand = 4096;
+constexpr int kRun = 16;  // elements per thread per streamed run
 
 // Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -61,8 +63,8 @@ __device__ int block_excl_scan(int v, int* wsum, int* total) {
   return off + x - v;
 }
 
-// Given counts h[0..nb) (nb <= 2 * 1024) and need >= 1, find the bin b with
-// count(bins > b) < need <= count(bins >= b).  Writes (*bin, *above).
+// Given counts h[0..nb) (nb <= 2048) and 1 <= need <= sum(h), find the bin b
+// with count(bins > b) < need <= count(bins >= b); writes (*bin, *above).
 __device__ void find_crossing(const int* h, int nb, int need, int* wsum, int* bin, int* above) {
   const int t = threadIdx.x;
   const int b0 = nb - 1 - 2 * t, b1 = b0 - 1;
@@ -74,18 +76,219 @@ __device__ void find_crossing(const int* h, int nb, int need, int* wsum, int* bi
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            int n, int k, int ld_scores,
-                                                            int32_t* __restrict__ idx,
-                                                            int ld_idx) {
-  __shared__ int hist[kBins];
-  __shared__ uint32_t ckey[kCand];
-  __shared__ int wsum[kTopkWaves];
-  __shared__ float red_min[kTopkWaves], red_max[kTopkWaves];
-  __shared__ int s_bin, s_above, s_cnt;
+constexpr int kCand = 4096;  // boundary-bin candidates kept in LDS
 
+struct TopkShared {
+  int hist[kBins];
+  uint32_t cand[kCand];
+  int wsum[kTopkWaves];
+  float red_min[kTopkWaves], red_max[kTopkWaves];
+  int bin, above, cnt;
+};
+
+// Load `N` consecutive scores starting at i0 (-inf past the end).
+template <int N>
+__device__ __forceinline__ void load_run(const float* s, int n, int i0, bool vec, float* x) {
+  if (vec && i0 + N <= n) {
+#pragma unroll
+    for (int m = 0; m < N / 4; ++m) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(s + i0 + 4 * m);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * m + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] = (i0 + e < n) ? s[i0 + e] : -INFINITY;
+  }
+}
+
+// Wave 0 finds the bin b of counts h[0..nb) (nb a multiple of 64) with
+// count(bins > b) < need <= count(bins >= b); writes (*bin, *above).  Lane l
+// owns the nb/64 bins counted downward from nb - 1 - l * nb/64.
+__device__ void wave_crossing(const int* h, int nb, int need, int* bin, int* above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb / 64;
+  const int top = nb - 1 - lane * per;
+  int sum = 0;
+  for (int q = 0; q < per; ++q) sum += h[top - q];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int ex = incl - sum;  // count of bins above this lane's range
+  if (ex < need && need <= incl) {
+    for (int q = 0; q < per; ++q) {
+      const int c = h[top - q];
+      if (need <= ex + c) {
+        *bin = top - q;
+        *above = ex;
+        break;
+      }
+      ex += c;
+    }
+  }
+}
+
+// Shared selection logic.  `visit(f)` calls f(value, index) for every slot of
+// the row owned by this thread, including the -inf padding past the end
+// (index >= n); `runs(g)` calls g(x, i0) for each owned run of RUN slots, in
+// increasing run order (runs with the same number are consecutive in the row
+// and ordered by thread id).  Padding is the smallest key: it may be counted
+// in a histogram but is never selected, because k <= n.
+template <int RUN, typename Visit, typename Runs>
+__device__ void select_row(TopkShared& sh, int n, int k, int32_t* out, Visit visit, Runs runs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) { s_bin = 0; s_above = 0; }
+
+  // 1. min / max over the real elements
+  float mn = INFINITY, mx = -INFINITY;
+  visit([&](float x, int i) {
+    mn = fminf(mn, i < n ? x : INFINITY);
+    mx = fmaxf(mx, x);
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) { sh.red_min[wave] = mn; sh.red_max[wave] = mx; }
+  for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+  if (tid == 0) { sh.cnt = 0; sh.bin = 0; sh.above = 0; }
+  __syncthreads();
+  mn = sh.red_min[0];
+  mx = sh.red_max[0];
+  for (int w = 1; w < kTopkWaves; ++w) { mn = fminf(mn, sh.red_min[w]); mx = fmaxf(mx, sh.red_max[w]); }
+  // equal-width bins between mn and mx (monotone in the value); a degenerate
+  // range puts everything in bin 0 and leaves the decision to the exact stage
+  float bscale = static_cast<float>(kBins) / (mx - mn);
+  if (!(bscale < INFINITY)) bscale = 0.f;
+  auto bin_of = [&](float x) {
+    const int b = static_cast<int>((x - mn) * bscale);
+    return max(0, min(b, kBins - 1));
+  };
+
+  // 2. value-bin histogram; wave 0 finds the boundary bin
+  visit([&](float x, int) { atomicAdd(&sh.hist[bin_of(x)], 1); });
+  __syncthreads();
+  if (wave == 0) wave_crossing(sh.hist, kBins, k, &sh.bin, &sh.above);
+  __syncthreads();
+  const int B = min(max(sh.bin, 0), kBins - 1);
+  int need = k - sh.above;  // elements still to take from bin B, >= 1
+
+  // 3. compact the boundary bin's real elements into LDS (wave ballots)
+  visit([&](float x, int i) {
+    const bool c = (i < n) & (bin_of(x) == B);
+    const unsigned long long bal = __ballot(c);
+    if (bal == 0ull) return;
+    const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&sh.cnt, __popcll(bal));
+    base = __shfl(base, 0);
+    const int slot = base + before;
+    if (c && slot < kCand) sh.cand[slot] = fkey(x);
+  });
+  __syncthreads();
+  const int ncand = sh.cnt;
+
+  // 4. exact threshold key tau: the need-th largest candidate key.  Up to one
+  //    candidate per thread: rank each against all; else 8-bit radix passes.
+  uint32_t tau;
+  if (ncand <= kTopkThreads) {
+    if (tid < ncand) {
+      const uint32_t mine = sh.cand[tid];
+      int gt = 0, eq = 0;
+      for (int c = 0; c < ncand; ++c) {
+        const uint32_t o = sh.cand[c];
+        gt += o > mine;
+        eq += o == mine;
+      }
+      if (gt < need && need <= gt + eq) {  // every holder of this key agrees
+        sh.bin = static_cast<int>(mine);
+        sh.above = gt;
+      }
+    }
+    __syncthreads();
+    tau = static_cast<uint32_t>(sh.bin);
+    need -= sh.above;
+  } else {
+    const bool in_lds = ncand <= kCand;
+    uint32_t prefix = 0, pmask = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (int c = tid; c < ncand; c += kTopkThreads) {
+          const uint32_t kx = sh.cand[c];
+          if ((kx & pmask) == prefix) atomicAdd(&sh.hist[(kx >> shift) & 255u], 1);
+        }
+      } else {
+        visit([&](float x, int i) {
+          if (i >= n || bin_of(x) != B) return;
+          const uint32_t kx = fkey(x);
+          if ((kx & pmask) == prefix) atomicAdd(&sh.hist[(kx >> shift) & 255u], 1);
+        });
+      }
+      __syncthreads();
+      if (wave == 0) wave_crossing(sh.hist, 256, need, &sh.bin, &sh.above);
+      __syncthreads();
+      need -= sh.above;
+      prefix |= static_cast<uint32_t>(min(max(sh.bin, 0), 255)) << shift;
+      pmask |= 0xffu << shift;
+      __syncthreads();
+    }
+    tau = prefix;
+  }
+
+  // 5. compaction in index order.  One scan of packed (greater, equal) counts
+  //    per run: the output position of a thread's first pick is
+  //    GT_before + min(need, EQ_before).
+  int base_gt = 0, base_eq = 0;
+  runs([&](const float* x, int i0) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < RUN; ++e) {
+      const uint32_t kx = fkey(x[e]);
+      gt += kx > tau;
+      eq += kx == tau;
+    }
+    int tot;
+    const int ex = block_excl_scan(gt | (eq << 16), sh.wsum, &tot);
+    const int gt_before = base_gt + (ex & 0xffff), eq_before = base_eq + (ex >> 16);
+    int take = need - eq_before;
+    take = take < 0 ? 0 : (take > eq ? eq : take);
+    if (gt + take > 0) {
+      int pos = gt_before + min(need, eq_before);
+      int eq_seen = 0;
+#pragma unroll
+      for (int e = 0; e < RUN; ++e) {
+        const uint32_t kx = fkey(x[e]);
+        bool pick = kx > tau;
+        if (kx == tau) {
+          pick = eq_seen < take;
+          ++eq_seen;
+        }
+        if (pick) {
+          if (pos < k) out[pos] = i0 + e;
+          ++pos;
+        }
+      }
+    }
+    base_gt += tot & 0xffff;
+    base_eq += tot >> 16;
+  });
+}
+
+// Rows of n <= 1024 * ITEMS: thread t owns [t * ITEMS, (t + 1) * ITEMS) in registers.
+template <int ITEMS>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __restrict__ scores,
+                                                                int n, int k, int ld_scores,
+                                                                int32_t* __restrict__ idx,
+                                                                int ld_idx) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
   const float* s = scores + static_cast<size_t>(blockIdx.x) * ld_scores;
   int32_t* out = idx + static_cast<size_t>(blockIdx.x) * ld_idx;
   if (k > n) k = n;
@@ -94,123 +297,52 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
     return;
   }
-
-  // 1. min / max
-  float mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const float x = s[i];
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
-  }
+  const bool vec = ((ld_scores & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  const int i0 = tid * ITEMS;
+  float x[ITEMS];
+  load_run<ITEMS>(s, n, i0, vec, x);
+  select_row<ITEMS>(
+      sh, n, k, out,
+      [&](auto f) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  if (lane == 0) { red_min[wave] = mn; red_max[wave] = mx; }
-  __syncthreads();
-  mn = red_min[0];
-  mx = red_max[0];
-  for (int w = 1; w < kTopkWaves; ++w) { mn = fminf(mn, red_min[w]); mx = fmaxf(mx, red_max[w]); }
+        for (int e = 0; e < ITEMS; ++e) f(x[e], i0 + e);
+      },
+      [&](auto g) { g(x, i0); });
+}
 
-  // bin width: value bins between mn and mx; a degenerate range puts every
-  // element in bin 0 and leaves the exact work to the radix select
-  float bscale = static_cast<float>(kBins) / (mx - mn);
-  if (!(bscale < INFINITY)) bscale = 0.f;
-  auto bin_of = [&](float x) {
-    int b = static_cast<int>((x - mn) * bscale);
-    return b < kBins - 1 ? b : kBins - 1;
+// Longer rows: runs of kRun elements per thread, super-tile r covering
+// [r * 1024 * kRun, (r + 1) * 1024 * kRun), re-read from L2 for every pass.
+__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(const float* __restrict__ scores,
+                                                                   int n, int k, int ld_scores,
+                                                                   int32_t* __restrict__ idx,
+                                                                   int ld_idx) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const float* s = scores + static_cast<size_t>(blockIdx.x) * ld_scores;
+  int32_t* out = idx + static_cast<size_t>(blockIdx.x) * ld_idx;
+  if (k > n) k = n;
+  if (k <= 0) return;
+  if (k == n) {
+    for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
+    return;
+  }
+  const bool vec = ((ld_scores & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  constexpr int kSuper = kTopkThreads * kRun;
+  auto runs = [&](auto g) {
+    for (int base = 0; base < n; base += kSuper) {
+      const int i0 = base + tid * kRun;
+      float x[kRun];
+      load_run<kRun>(s, n, i0, vec, x);
+      g(x, i0);
+    }
   };
-
-  // 2. histogram of value bins
-  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) atomicAdd(&hist[bin_of(s[i])], 1);
-  __syncthreads();
-  find_crossing(hist, kBins, k, wsum, &s_bin, &s_above);
-  const int B = min(max(s_bin, 0), kBins - 1), above = s_above;
-  const int in_b = hist[B];
-  const int need0 = k - above;  // 1 .. in_b
-  __syncthreads();
-
-  // 3. exact threshold inside bin B
-  const bool use_lds = in_b <= kCand;
-  if (tid == 0) s_cnt = 0;
-  __syncthreads();
-  if (use_lds) {
-    for (int i = tid; i < n; i += kTopkThreads) {
-      const float x = s[i];
-      if (bin_of(x) == B) {
-        const int slot = atomicAdd(&s_cnt, 1);
-        if (slot < kCand) ckey[slot] = fkey(x);
-      }
-    }
-    __syncthreads();
-  }
-  uint32_t prefix = 0, pmask = 0;
-  int need = need0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    if (use_lds) {
-      for (int c = tid; c < in_b; c += kTopkThreads) {
-        const uint32_t kx = ckey[c];
-        if ((kx & pmask) == prefix) atomicAdd(&hist[(kx >> shift) & 255u], 1);
-      }
-    } else {
-      for (int i = tid; i < n; i += kTopkThreads) {
-        const float x = s[i];
-        if (bin_of(x) != B) continue;
-        const uint32_t kx = fkey(x);
-        if ((kx & pmask) == prefix) atomicAdd(&hist[(kx >> shift) & 255u], 1);
-      }
-    }
-    __syncthreads();
-    find_crossing(hist, 256, need, wsum, &s_bin, &s_above);
-    need -= s_above;
-    prefix |= static_cast<uint32_t>(s_bin) << shift;
-    pmask |= 0xffu << shift;
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;  // the threshold key; `need` elements equal to it are taken
-
-  // 4. compaction in index order, 4 consecutive elements per thread per tile
-  int base_sel = 0, base_eq = 0;
-  for (int t0 = 0; t0 < n; t0 += 4 * kTopkThreads) {
-    const int i0 = t0 + 4 * tid;
-    uint32_t kx[4];
-    int gt = 0, eq = 0;
+  auto visit = [&](auto f) {
+    runs([&](const float* x, int i0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kx[e] = (i0 + e < n) ? fkey(s[i0 + e]) : 0u;
-      const bool valid = i0 + e < n;
-      gt += valid & (kx[e] > tau);
-      eq += valid & (kx[e] == tau);
-    }
-    int tot_eq, tot_sel;
-    const int eq_rank = base_eq + block_excl_scan(eq, wsum, &tot_eq);
-    int take = need - eq_rank;
-    take = take < 0 ? 0 : (take > eq ? eq : take);
-    const int pos0 = base_sel + block_excl_scan(gt + take, wsum, &tot_sel);
-    int pos = pos0, eq_seen = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e >= n) break;
-      if (kx[e] > tau) {
-        if (pos < k) out[pos] = i0 + e;
-        ++pos;
-      } else if (kx[e] == tau) {
-        if (eq_seen < take) {
-          if (pos < k) out[pos] = i0 + e;
-          ++pos;
-        }
-        ++eq_seen;
-      }
-    }
-    base_eq += tot_eq;
-    base_sel += tot_sel;
-  }
+      for (int e = 0; e < kRun; ++e) f(x[e], i0 + e);
+    });
+  };
+  select_row<kRun>(sh, n, k, out, visit, runs);
 }
 
 }  // namespace
@@ -218,8 +350,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
                        int ld_idx, hipStream_t st) {
   if (rows == 0 || n == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), 0, st, scores, n, k, ld_scores,
-                     idx, ld_idx);
+  const dim3 grid(rows), block(kTopkThreads);
+  if (n <= 4 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg_kernel<4>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+  else if (n <= 8 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+  else if (n <= 16 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg_kernel<16>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+  else
+    hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
   return hipGetLastError();
 }
 

@@ -58,3 +58,17 @@ def assert_sorted_unique(idx_row, n):
 
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np64(a) - np64(b)))) if np.asarray(np64(a)).size else 0.0
+
+
+def group_agreement(gpu_qidx, ref_qidx, G):
+    """(b, nkv) bool: True where every head of the KV group kept the same
+    queries in the same rank order on both sides.  Slot n of the group mean
+    pairs the n-th ranked query of each head, so where two queries of a head
+    are within rounding of each other the two sides may legitimately pair
+    differently; downstream scores of such a group are then not comparable
+    value by value (the query choice itself is checked by the boundary rule)."""
+    g = np.asarray(gpu_qidx)
+    r = np.asarray(ref_qidx)
+    b, nq, _ = g.shape
+    same = np.all(g == r, axis=-1).reshape(b, nq // G, G)
+    return np.all(same, axis=-1)
