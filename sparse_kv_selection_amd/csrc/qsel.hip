@@ -7,11 +7,11 @@
 //
 // Two kernels, both latency-bound (the chunk is a few MiB at most):
 //   1. one workgroup per query head: every thread owns one 16-byte column
-//      chunk of a strided set of rows, so all row loads of a pass are in flight
-//      at once; the mean is a column sum reduced through LDS, the per-row dot
-//      products and norms are reduced across the lanes that share a row, and
-//      the top-NQ is a rank count in LDS (number of queries that beat query i,
-//      ties going to the lower position) -- exact and deterministic;
+//      chunk of a strided set of rows, held in registers so all row loads are
+//      in flight at once; the mean is a column sum reduced through LDS, the
+//      per-row dot products and norms are reduced across the lanes that share
+//      a row, and one wave sorts the (score, position) keys with a bitonic
+//      network -- exact, deterministic, ties to the lower position;
 //   2. one wave per (sequence, KV head, slot n): the n-th kept query of each of
 //      the G heads is normalised and the G unit vectors are averaged in a fixed
 //      order.
@@ -20,26 +20,6 @@
 
 namespace qk {
 namespace {
-
-constexpr int kHeadThreads = 1024;
-constexpr int kRankSplit = 4;  // lanes sharing one row's rank count
-
-template <typename T> struct Chunk8;  // 8 consecutive elements as fp32
-template <> struct Chunk8<uint16_t> {
-  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
-    const u32x4 w = ld16(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo(w[e]); x[2 * e + 1] = bf16hi(w[e]); }
-  }
-};
-template <> struct Chunk8<float> {
-  __device__ __forceinline__ static void load(const float* p, float* x) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
-  }
-};
 
 // Raw 8-element chunk kept in registers between passes.
 template <typename T> struct Raw8;
@@ -65,101 +45,146 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void zero() { a = f32x4{}; b = f32x4{}; }
 };
 
-// rank of position i among the scores sq[0..n4*4) (padded with -inf): the
-// number of entries larger than s, or equal to it at a lower position
-__device__ __forceinline__ int rank_of(const float* sq, int n4, int i, float s) {
-  const f32x4* sq4 = reinterpret_cast<const f32x4*>(sq);
-  int rank = 0;
-#pragma unroll 4
-  for (int i4 = 0; i4 < n4; ++i4) {
-    const f32x4 v = sq4[i4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rank += (v[e] > s) | ((v[e] == s) & (4 * i4 + e < i));
-  }
-  return rank;
+// Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
+__device__ __forceinline__ uint32_t okey(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// mq[e] = (sum over r < NRL of part[r][e]) / bcp: S = 1024 / D consecutive
-// lanes share column e, each summing NRL / S partials, then a shuffle sum.
-template <int D, int NRL>
-__device__ __forceinline__ void column_mean(const float* part, float* mq, int bcp) {
-  constexpr int S = kHeadThreads / D;
-  static_assert(NRL % S == 0 && 64 % S == 0, "column split");
-  const int tid = threadIdx.x;
-  const int e = tid / S, j = tid % S;
-  float sum = 0.f;
-#pragma unroll 4
-  for (int r = j; r < NRL; r += S) sum += part[r * D + e];
+// One wave sorts P = 64 * E packed keys descending (bitonic network); lane l
+// holds positions [l * E, (l + 1) * E).  Key = (score key << 32) | ~position,
+// so larger scores come first and equal scores keep the lower position first.
+template <int E>
+__device__ void wave_sort_desc(uint64_t* v) {
+  const int lane = threadIdx.x & 63;
+  constexpr int P = 64 * E;
 #pragma unroll
-  for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o);
-  if (j == 0) mq[e] = sum / static_cast<float>(bcp);
-}
-
-// Top-NQ by rank, kRankSplit consecutive lanes per position: each counts over
-// a quarter of the scores and the partial counts are summed with shuffles.
-__device__ __forceinline__ void rank_and_store(const float* sq, int n4, int bcp, int nq_keep,
-                                               int32_t* out) {
-  const int tid = threadIdx.x;
-  const int part = tid % kRankSplit;
-  const int per4 = (n4 + kRankSplit - 1) / kRankSplit;
-  const int lo4 = part * per4, hi4 = min(n4, lo4 + per4);
-  for (int i0 = 0; i0 < bcp; i0 += kHeadThreads / kRankSplit) {
-    const int i = i0 + tid / kRankSplit;
-    const float s = i < bcp ? sq[i] : -INFINITY;
-    const f32x4* sq4 = reinterpret_cast<const f32x4*>(sq);
-    int rank = 0;
-#pragma unroll 4
-    for (int i4 = lo4; i4 < hi4; ++i4) {
-      const f32x4 v = sq4[i4];
+  for (int kk = 2; kk <= P; kk <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rank += (v[e] > s) | ((v[e] == s) & (4 * i4 + e < i));
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pe = e ^ j;
+          if (pe > e) {
+            const int i = lane * E + e;
+            const bool desc_block = (i & kk) == 0;  // this block sorts descending
+            const uint64_t a = v[e], c = v[pe];
+            const bool swap = desc_block ? (a < c) : (a > c);
+            v[e] = swap ? c : a;
+            v[pe] = swap ? a : c;
+          }
+        }
+      } else {
+        const int lx = j / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = lane * E + e;
+          const uint64_t o = __shfl_xor(v[e], lx);
+          const bool lower = (i & j) == 0;
+          const bool desc_block = (i & kk) == 0;
+          // the lower position of a descending block keeps the larger key
+          const bool keep_max = lower == desc_block;
+          v[e] = keep_max ? (v[e] > o ? v[e] : o) : (v[e] < o ? v[e] : o);
+        }
+      }
     }
-#pragma unroll
-    for (int o = 1; o < kRankSplit; o <<= 1) rank += __shfl_xor(rank, o);
-    if (part == 0 && i < bcp && rank < nq_keep) out[rank] = i;
   }
 }
 
-// Every row of the head is read once into registers (RPT rows per thread).
-template <typename T, int D, int RPT>
-__global__ __launch_bounds__(kHeadThreads) void qsel_head_reg_kernel(const T* __restrict__ q,
-                                                                     int32_t* __restrict__ q_idx,
-                                                                     float* __restrict__ sq_out,
-                                                                     int bcp, int nq_keep) {
-  constexpr int CH = D / 8;
-  constexpr int NRL = kHeadThreads / CH;
+// Wave 0 of the block: top-NQ positions of sq[0..bcp) by decreasing score.
+template <int E>
+__device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane * E + e;
+    v[e] = i < bcp ? (static_cast<uint64_t>(okey(sq[i])) << 32) | static_cast<uint32_t>(~i) : 0ull;
+  }
+  wave_sort_desc<E>(v);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = lane * E + e;
+    if (p < nq_keep) out[p] = static_cast<int32_t>(~static_cast<uint32_t>(v[e]));
+  }
+}
+
+// Longer chunks (no wave sort): rank of every position by counting the
+// scores that beat it (larger, or equal at a lower position), NT threads.
+template <int NT>
+__device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_t* out) {
+  for (int i = threadIdx.x; i < bcp; i += NT) {
+    const float s = sq[i];
+    int rank = 0;
+    for (int i2 = 0; i2 < bcp; ++i2) {
+      const float s2 = sq[i2];
+      rank += (s2 > s) | ((s2 == s) & (i2 < i));
+    }
+    if (rank < nq_keep) out[rank] = i;
+  }
+}
+
+// One workgroup of NT threads per query head.  Thread (row lane r, chunk c)
+// owns the 8-element chunk c of rows r, r + NT / CH, ...; RPT > 0: all of
+// them held in registers (one memory trip); RPT == 0: two passes over memory.
+// E > 0: wave 0 sorts 64 * E >= bcp keys; E == 0: rank count instead.
+template <typename T, int D, int NT, int RPT, int E>
+__global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
+                                                       int32_t* __restrict__ q_idx,
+                                                       float* __restrict__ sq_out, int bcp,
+                                                       int nq_keep) {
+  constexpr int CH = D / 8;          // chunks per row (CH divides 64)
+  constexpr int NRL = NT / CH;       // rows handled at once
+  constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
   extern __shared__ float smem[];
-  float* part = smem;                        // [NRL][D]
-  float* mq = part + NRL * D;                // [D]
-  float* sq = mq + D;                        // [bcp rounded up to 4]
+  float* part = smem;                // [NRL][D]
+  float* mq = part + NRL * D;        // [D]
+  float* sq = mq + D;                // [bcp]
   __shared__ float s_mq2;
   const int tid = threadIdx.x;
   const int c = tid % CH, rl = tid / CH;
   const int bh = blockIdx.x;
   const T* qh = q + static_cast<size_t>(bh) * bcp * D;
-  const int n4 = (bcp + 3) / 4;
 
-  Raw8<T> rows[RPT];
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int i = u * NRL + rl;
-    if (i < bcp) rows[u].load(qh + static_cast<size_t>(i) * D + 8 * c);
-    else rows[u].zero();
-  }
-  for (int i = bcp + tid; i < 4 * n4; i += kHeadThreads) sq[i] = -INFINITY;
-
+  Raw8<T> rows[RPT > 0 ? RPT : 1];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (RPT > 0) {
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    float x[8];
-    rows[u].get(x);
+    for (int u = 0; u < RPT; ++u) {
+      const int i = u * NRL + rl;
+      if (i < bcp) rows[u].load(qh + static_cast<size_t>(i) * D + 8 * c);
+      else rows[u].zero();
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    for (int u = 0; u < RPT; ++u) {
+      float x[8];
+      rows[u].get(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+  } else {
+    for (int i = rl; i < bcp; i += NRL) {
+      Raw8<T> r;
+      r.load(qh + static_cast<size_t>(i) * D + 8 * c);
+      float x[8];
+      r.get(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rl * D + 8 * c + e] = acc[e];
   __syncthreads();
-  column_mean<D, NRL>(part, mq, bcp);
+  // mean query: S lanes per column, NRL / S partials each, then a shuffle sum
+  for (int col = tid / S; col < D; col += NT / S) {
+    float sum = 0.f;
+    for (int r = tid % S; r < NRL; r += S) sum += part[r * D + col];
+#pragma unroll
+    for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o);
+    if (tid % S == 0) mq[col] = sum / static_cast<float>(bcp);
+  }
   __syncthreads();
   if (tid < 64) {
     float m2 = 0.f;
@@ -172,11 +197,9 @@ __global__ __launch_bounds__(kHeadThreads) void qsel_head_reg_kernel(const T* __
   float m8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) m8[e] = mq[8 * c + e];
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int i = u * NRL + rl;
-    float x[8];
-    rows[u].get(x);
+
+  // SQ per row: the CH lanes of a row sit in one wave
+  auto score_row = [&](int i, const float* x) {
     float dot = 0.f, n2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { dot += x[e] * m8[e]; n2 += x[e] * x[e]; }
@@ -190,105 +213,33 @@ __global__ __launch_bounds__(kHeadThreads) void qsel_head_reg_kernel(const T* __
       sq[i] = sc;
       if (sq_out) sq_out[static_cast<size_t>(bh) * bcp + i] = sc;
     }
-  }
-  __syncthreads();
-  rank_and_store(sq, n4, bcp, nq_keep, q_idx + static_cast<size_t>(bh) * nq_keep);
-}
-
-// Chunks too long for registers: two passes over global memory (L2).
-template <typename T, int D>
-__global__ __launch_bounds__(kHeadThreads) void qsel_head_kernel(const T* __restrict__ q,
-                                                                 int32_t* __restrict__ q_idx,
-                                                                 float* __restrict__ sq_out,
-                                                                 int bcp, int nq_keep) {
-  constexpr int CH = D / 8;                  // 8-element chunks per row
-  constexpr int NRL = kHeadThreads / CH;     // rows handled at once
-  extern __shared__ float smem[];
-  float* part = smem;                        // [NRL][D] column partial sums
-  float* mq = part + NRL * D;                // [D]
-  float* sq = mq + D;                        // [bcp]
-  __shared__ float s_mq2;
-
-  const int tid = threadIdx.x;
-  const int c = tid % CH, rl = tid / CH;
-  const int bh = blockIdx.x;                 // (b, h)
-  const T* qh = q + static_cast<size_t>(bh) * bcp * D;
-  const int n4 = (bcp + 3) / 4;
-  for (int i = bcp + tid; i < 4 * n4; i += kHeadThreads) sq[i] = -INFINITY;
-
-  // mean query: column sums over strided rows (kBatch rows' loads in flight
-  // per thread), then over the NRL partials
-  constexpr int kBatch = 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i0 = 0; i0 < bcp; i0 += kBatch * NRL) {
-    float x[kBatch][8];
+  };
+  if constexpr (RPT > 0) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * NRL + rl;
+    for (int u = 0; u < RPT; ++u) {
+      float x[8];
+      rows[u].get(x);
+      score_row(u * NRL + rl, x);
+    }
+  } else {
+    for (int i0 = 0; i0 < bcp; i0 += NRL) {
+      const int i = i0 + rl;
+      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (i < bcp) {
-        Chunk8<T>::load(qh + static_cast<size_t>(i) * D + 8 * c, x[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+        Raw8<T> r;
+        r.load(qh + static_cast<size_t>(i) * D + 8 * c);
+        r.get(x);
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[u][e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rl * D + 8 * c + e] = acc[e];
-  __syncthreads();
-  column_mean<D, NRL>(part, mq, bcp);
-  __syncthreads();
-  if (tid < 64) {
-    float m2 = 0.f;
-    for (int e = tid; e < D; e += 64) m2 += mq[e] * mq[e];
-    m2 = wave_sum(m2);
-    if (tid == 0) s_mq2 = m2;
-  }
-  __syncthreads();
-  const float mq_norm = fmaxf(sqrtf(s_mq2), kEps);
-  float m8[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m8[e] = mq[8 * c + e];
-
-  // SQ per row: CH lanes share a row (CH divides 64, so they share a wave)
-  for (int i0 = 0; i0 < bcp; i0 += kBatch * NRL) {
-    float x[kBatch][8];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * NRL + rl;
-      if (i < bcp) {
-        Chunk8<T>::load(qh + static_cast<size_t>(i) * D + 8 * c, x[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * NRL + rl;
-      float dot = 0.f, n2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { dot += x[u][e] * m8[e]; n2 += x[u][e] * x[u][e]; }
-#pragma unroll
-      for (int o = CH / 2; o > 0; o >>= 1) {
-        dot += __shfl_xor(dot, o);
-        n2 += __shfl_xor(n2, o);
-      }
-      if (c == 0 && i < bcp) {
-        const float s = -dot / (fmaxf(sqrtf(n2), kEps) * mq_norm);
-        sq[i] = s;
-        if (sq_out) sq_out[static_cast<size_t>(bh) * bcp + i] = s;
-      }
+      score_row(i, x);
     }
   }
   __syncthreads();
-
-  // top-NQ by rank
-  rank_and_store(sq, n4, bcp, nq_keep, q_idx + static_cast<size_t>(bh) * nq_keep);
+  int32_t* out = q_idx + static_cast<size_t>(bh) * nq_keep;
+  if constexpr (E > 0) {
+    if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out);
+  } else {
+    top_positions_rank<NT>(sq, bcp, nq_keep, out);
+  }
 }
 
 // One wave per (b, j, n): mean over the group's heads of the unit n-th kept query.
@@ -337,20 +288,39 @@ __global__ __launch_bounds__(64) void qgroup_kernel(const T* __restrict__ q,
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = acc[e] * inv_g;
 }
 
+template <typename T, int D, int NT, int RPT>
+void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bcp, int nq_keep,
+                 hipStream_t st) {
+  constexpr int NRL = NT / (D / 8);
+  const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
+  const dim3 grid(b * nq), block(NT);
+  const T* qq = static_cast<const T*>(q);
+#define QK_HEAD(EE) \
+  hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, EE>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep)
+  if (bcp <= 64) QK_HEAD(1);
+  else if (bcp <= 128) QK_HEAD(2);
+  else if (bcp <= 256) QK_HEAD(4);
+  else if (bcp <= 512) QK_HEAD(8);
+  else if (bcp <= 1024) QK_HEAD(16);
+  else QK_HEAD(0);
+#undef QK_HEAD
+}
+
 template <typename T, int D>
 hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, int nq, int nkv,
                int bcp, int nq_keep, hipStream_t st) {
-  constexpr int NRL = kHeadThreads / (D / 8);
-  const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + 4 * ((bcp + 3) / 4));
-  const int rpt = (bcp + NRL - 1) / NRL;
-  const T* qq = static_cast<const T*>(q);
-  const dim3 grid(b * nq), block(kHeadThreads);
-  if (rpt <= 2)
-    hipLaunchKernelGGL((qsel_head_reg_kernel<T, D, 2>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
-  else if (rpt <= 8)
-    hipLaunchKernelGGL((qsel_head_reg_kernel<T, D, 8>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
-  else
-    hipLaunchKernelGGL((qsel_head_kernel<T, D>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  constexpr int CH = D / 8;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  if (bcp * CH <= 64) {
+    launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, st);   // decode-sized chunks
+  } else {
+    constexpr int NRL = 256 / CH;
+    const int rpt = (bcp + NRL - 1) / NRL;
+    if (rpt <= 4) launch_head<T, D, 256, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    else if (rpt <= 16) launch_head<T, D, 256, 16>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    else if (kBf16 && rpt <= 32) launch_head<T, D, 256, (kBf16 ? 32 : 16)>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    else launch_head<T, D, 256, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+  }
   hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
                      static_cast<const T*>(q), q_idx, q_group, nq, nkv, bcp, nq_keep);
   return hipGetLastError();
