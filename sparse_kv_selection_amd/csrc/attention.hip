@@ -56,23 +56,54 @@ struct AttnParams {
 };
 
 constexpr int kKeyTile = 64;
+constexpr float kSlack = 8.f;  // lazy-rescale slack, base-2 exponent units
 
-template <int D, int NB, int WAVES, int OCC>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS; the wave's 64 lanes
+// fill 1 KiB at lds (wave-uniform) in lane order.
+__device__ __forceinline__ void lds_load16(const uint16_t* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// Two transposed 8-byte LDS reads (rows p and p + 8 * stride) as one 8-slot
+// matrix-core operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint16_t* p, int stride) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * stride));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 16-byte chunk swizzles of the K and V tiles in LDS.  Chunk c of tile row r
+// is stored at chunk position c ^ swz(r); the functions spread the matrix-core
+// reads over all LDS banks (row reads of K, transposed reads of V).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+}
+
+template <int D, int WAVES, int OCC, bool IDX>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int ROWS = WAVES * NB * 32;
-  constexpr int KSTR = D + 8;          // sK row stride, elements
-  constexpr int VSTR = kKeyTile + 8;   // sVT row stride, elements
-  constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int KUNITS = kKeyTile * CH;
-  constexpr int VUNITS = 16 * CH;      // units of 4 rows x 16 bytes
-  constexpr int KPER = (KUNITS + NT - 1) / NT;
-  constexpr int VPER = (VUNITS + NT - 1) / NT;
-  constexpr bool kPrefetch = true;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeyTile * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sVT[D * VSTR];
+  constexpr int ROWS = WAVES * 32;
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;                // tile rows per wave-wide 16-byte load
+  constexpr int IPW = kKeyTile / (RPI * WAVES);  // such loads per wave per matrix
+  constexpr int TILE = kKeyTile * D;          // elements per K (or V) tile
+  static_assert(IPW >= 1 && IPW * RPI * WAVES == kKeyTile, "tile split");
+  // two stages (double buffer), separate objects so that the compiler sees
+  // that reads of one stage do not alias the loads in flight into the other
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int L = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -85,7 +116,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   const int M = G * bcp;
 
   // past rows available: the index list length, or the rows of the past buffer
-  const int past_cap = p.idx ? p.ld_idx : static_cast<int>(p.past_bj_rows);
+  const int past_cap = IDX ? p.ld_idx : static_cast<int>(p.past_bj_rows);
   // wave-uniform (readfirstlane): tile classification below branches on it
   const int n_past =
       __builtin_amdgcn_readfirstlane(min(p.sel_len ? p.sel_len[bj] : p.n_past, past_cap));
@@ -105,229 +136,217 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   const uint16_t* pv = p.pv + static_cast<size_t>(bj) * p.past_bj_rows * D;
   const uint16_t* ck = p.k + (static_cast<size_t>(bj) * p.kv_cap + p.t_past) * D;
   const uint16_t* cv = p.v + (static_cast<size_t>(bj) * p.kv_cap + p.t_past) * D;
-  const int32_t* idx = p.idx ? p.idx + static_cast<size_t>(bj) * p.ld_idx : nullptr;
+  const int32_t* idx = IDX ? p.idx + static_cast<size_t>(bj) * p.ld_idx : nullptr;
   const int row_hi = static_cast<int>(p.past_bj_rows) - 1;
 
-  // Element offset of tile key r.  Keys past the end of the range are clamped
-  // onto a valid row: they are masked to -inf, so their weight is exactly 0.
-  auto key_off = [&](int t, int r) -> int {
-    if (t < npt) {
-      const int kk = min((pt0 + t) * kKeyTile + r, n_past - 1);
-      const int row = idx ? min(max(idx[kk], 0), row_hi) : kk;
-      return row * D;
+  // ---- tile loads: global -> LDS directly, 16 bytes per lane ----
+  // Load i of this wave fills tile rows (wave * IPW + i) * RPI + [0, RPI); lane
+  // l writes chunk position l % CH of row r = ... + l / CH and so fetches the
+  // global chunk (l % CH) ^ swz(r) of that key's row.
+  int trow[IPW];     // tile row of each load of this lane
+  int kchunk[IPW];   // element offset of the fetched chunk, K
+  int vchunk[IPW];   // element offset of the fetched chunk, V
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * RPI + lane / CH;
+    trow[i] = r;
+    kchunk[i] = 8 * ((lane % CH) ^ swz_k<D>(r));
+    vchunk[i] = 8 * ((lane % CH) ^ swz_v<D>(r));
+  }
+  // Key rows of a tile.  Keys past the end of the range are clamped onto a
+  // valid row; they are masked to -inf, so their weight is exactly 0.  Index
+  // entries are loaded one tile ahead of the data loads that use them.
+  int krow[IPW];
+  auto rows_of = [&](int t) {
+    if (t < npt) {  // uniform
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int kk = min((pt0 + t) * kKeyTile + trow[i], n_past - 1);
+        krow[i] = IDX ? idx[kk] : kk;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) krow[i] = min((t - npt) * kKeyTile + trow[i], bcp - 1);
     }
-    return min((t - npt) * kKeyTile + r, bcp - 1) * D;
+  };
+  auto issue = [&](int t, uint16_t* dK, uint16_t* dV) {
+    const bool past = t < npt;
+    const uint16_t* kbase = past ? pk : ck;
+    const uint16_t* vbase = past ? pv : cv;
+    const int hi = past ? row_hi : bcp - 1;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const uint32_t ro = static_cast<uint32_t>(min(max(krow[i], 0), hi)) * D;
+      uint16_t* lk = dK + (wave * IPW + i) * 512;
+      uint16_t* lv = dV + (wave * IPW + i) * 512;
+      lds_load16(kbase + ro + kchunk[i], lk);
+      lds_load16(vbase + ro + vchunk[i], lv);
+    }
   };
 
-  // query fragments: lane (col, half) holds row col of block nb, d slots 16s + 8half + [0,8)
-  bf16x8 qf[NB][D / 16];
-  int iq[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int r = row0 + (wave * NB + nb) * 32 + col;
+  // query fragments: lane (col, half) holds row col, d slots 16s + 8half + [0,8)
+  bf16x8 qf[D / 16];
+  int iq;
+  {
+    const int r = row0 + wave * 32 + col;
     const bool valid = r < M;
     const int i = r / G, g = r - (r / G) * G;
-    iq[nb] = i;
+    iq = i;
     const uint16_t* qp = p.q + ((static_cast<size_t>(b) * p.nq + j * G + g) * bcp + i) * D;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qf[nb][s] = valid ? as_bf16x8(ld16(qp + 16 * s + 8 * half)) : bf16x8{};
+      qf[s] = valid ? as_bf16x8(ld16(qp + 16 * s + 8 * half)) : bf16x8{};
   }
-
   // a wave whose rows are all padding only helps with the tile loads
-  const bool wave_active = row0 + wave * NB * 32 < M;
+  const bool wave_active = row0 + wave * 32 < M;
 
-  f32x16 acc[NB][D / 32];
-  float m_run[NB], l_run[NB];
+  // LDS read offsets (elements).  K: lane (col, half), step s reads row
+  // kb*32 + col, chunk 2s + half -> position (2s) ^ fk with fk = half ^ swz.
+  constexpr int NKA = D / 16 < 8 ? D / 16 : 8;
+  int kofs[NKA];
+  {
+    const int fk = half ^ swz_k<D>(col);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
+    for (int s = 0; s < NKA; ++s) kofs[s] = col * D + 8 * ((2 * s) ^ fk);
+  }
+  // V (transposed reads, 16-lane groups): lane (g = lane/16, jl = lane%16)
+  // addresses row 4*(g/2) + jl/4 (+16 g16 + 8 q), columns 32 db + 16 (g%2) +
+  // 4 (jl%4) + [0,4); the hardware hands lane i of the group element i%4 of
+  // group lane 4k + i/4 as its k-th value, i.e. keys 4*(g/2) + [0,4) (+8 q) of
+  // column 32 db + 16 (g%2) + i: the B-operand key order of P below.
+  int vofs[D / 32];
+  {
+    const int g = lane >> 4, jl = lane & 15, jj = jl >> 2;
+    const int vr = 4 * (g >> 1) + jj;
+    const int x = 2 * (g & 1) + ((jl & 3) >> 1);
+    const int fv = swz_v<D>(vr);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[nb][db] = f32x16{};
+    for (int db = 0; db < D / 32; ++db)
+      vofs[db] = vr * D + 8 * ((4 * db + x) ^ fv) + 4 * (jl & 1);
   }
 
-  // Tile loads.  Offsets for tile t+1 are computed (index loads) while tile t
-  // is in flight, so index and data loads never wait on each other.
-  int koff[KPER], voff[VPER][4];
-  u32x4 kreg[KPER];
-  u32x4 vreg[VPER][4];
-  auto offsets = [&](int t) {
+  f32x16 acc[D / 32];
+  float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < KPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (KUNITS % NT == 0 || u < KUNITS) koff[pp] = key_off(t, u / CH) + 8 * (u % CH);
-    }
-#pragma unroll
-    for (int pp = 0; pp < VPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int sg = u & 15, c = u >> 4;
-        const int q4 = sg & 3;
-        const int kb4 = (sg >> 2) * 16 + (q4 & 1) * 8 + (q4 >> 1) * 4;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) voff[pp][e4] = key_off(t, kb4 + e4) + 8 * c;
-      }
-    }
-  };
-  auto fetch = [&](int t) {
-    const uint16_t* kbase = t < npt ? pk : ck;
-    const uint16_t* vbase = t < npt ? pv : cv;
-#pragma unroll
-    for (int pp = 0; pp < KPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (KUNITS % NT == 0 || u < KUNITS) kreg[pp] = ld16(kbase + koff[pp]);
-    }
-#pragma unroll
-    for (int pp = 0; pp < VPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) vreg[pp][e4] = ld16(vbase + voff[pp][e4]);
-      }
-    }
-  };
-
-  auto store = [&]() {
-#pragma unroll
-    for (int pp = 0; pp < KPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (KUNITS % NT == 0 || u < KUNITS) {
-        const int r = u / CH, c = u - (u / CH) * CH;
-        st16(sK + r * KSTR + 8 * c, kreg[pp]);
-      }
-    }
-#pragma unroll
-    for (int pp = 0; pp < VPER; ++pp) {
-      const int u = tid + pp * NT;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int sg = u & 15, c = u >> 4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          uint32_t d0, d1;
-          if ((e & 1) == 0) {
-            d0 = (vreg[pp][0][w] & 0xffffu) | (vreg[pp][1][w] << 16);
-            d1 = (vreg[pp][2][w] & 0xffffu) | (vreg[pp][3][w] << 16);
-          } else {
-            d0 = (vreg[pp][0][w] >> 16) | (vreg[pp][1][w] & 0xffff0000u);
-            d1 = (vreg[pp][2][w] >> 16) | (vreg[pp][3][w] & 0xffff0000u);
-          }
-          uint2 pr;
-          pr.x = d0;
-          pr.y = d1;
-          *reinterpret_cast<uint2*>(sVT + (8 * c + e) * VSTR + 4 * sg) = pr;
-        }
-      }
-    }
-  };
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   const float c2 = p.scale_log2;
-  if (n_tiles > 0) {
-    offsets(0);
-    fetch(0);
-    if (n_tiles > 1) offsets(1);
-  }
-  auto tile = [&](int t, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (kPrefetch && t + 1 < n_tiles) {
-      fetch(t + 1);
-      if (t + 2 < n_tiles) offsets(t + 2);
-    }
-    if (!wave_active) return;
 
-    // S^T = K Q^T for 64 keys x (NB * 32) queries
-    f32x16 S[2][NB];
+  const int n_full = min(max(n_past / kKeyTile - pt0, 0), npt);
+  auto compute = [&](int t, const uint16_t* cK, const uint16_t* cV) {
+    // S^T = K Q^T for 64 keys x 32 queries
+    f32x16 S[2];
+    S[0] = f32x16{};
+    S[1] = f32x16{};
+    // K fragments are read one d-step ahead of the products that use them
+    auto kfrag = [&](int s, int kb) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(cK + kb * 32 * D + kofs[s % NKA] +
+                                                       128 * (s / NKA)));
+    };
+    bf16x8 ka0 = kfrag(0, 0), ka1 = kfrag(0, 1);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 c0 = ka0, c1 = ka1;
+      if (s + 1 < D / 16) {
+        ka0 = kfrag(s + 1, 0);
+        ka1 = kfrag(s + 1, 1);
+      }
+      S[0] = mfma32(c0, qf[s], S[0]);
+      S[1] = mfma32(c1, qf[s], S[1]);
+    }
+    const bool is_chunk = t >= npt;
+    const int kbase = is_chunk ? (t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
+    if (t >= n_full) {  // uniform: boundary and chunk tiles only
+      // key kbase + 32 kb + acc_row(r, half) is masked when it reaches the limit;
+      // the lane's offset is folded into one bound, the rest are immediates
+      const int lim = (is_chunk ? min(bcp, iq + 1) : n_past) - kbase - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) S[kb][r] = -INFINITY;
+    }
+    float mx = S[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) S[kb][nb] = f32x16{};
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    // Lazy rescale: the running maximum only moves when the tile's maximum
+    // exceeds it by more than kSlack (base 2), so probabilities stay below
+    // 2^kSlack and the accumulator is rescaled on few tiles.  The result is
+    // the same softmax: numerator and denominator share the reference.
+    float alpha = 1.f;
+    if (__any(mx > m_run + kSlack)) {
+      const float m_new = mx > m_run + kSlack ? mx : m_run;
+      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(sK + (kb * 32 + col) * KSTR + 16 * s + 8 * half));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) S[kb][nb] = mfma32(a, qf[nb][s], S[kb][nb]);
-      }
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
     }
-
-    // mask (boundary and chunk tiles only), online softmax in base 2
-    const bool is_chunk = t >= npt;
-    const int kbase = is_chunk ? (t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
-    bf16x8 P[NB][4];
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // P^T operand: lane half h, 16-key group g16, slot e <-> key
+    // 16 g16 + 8 (e / 4) + 4 h + e % 4 (the accumulator row order of S^T)
+    bf16x8 P[4];
+    float ps = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (kMasked) {
-          const int klimit = is_chunk ? min(bcp, iq[nb] + 1) : n_past;
+    for (int g16 = 0; g16 < 4; ++g16) {
+      const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
+      u32x4 w;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kbase + kb * 32 + acc_row(r, half) >= klimit) S[kb][nb][r] = -INFINITY;
-        }
-        float mx = S[0][nb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][nb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-        const float m_new = fmaxf(m_run[nb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
-        m_run[nb] = m_new;
-        float ps = 0.f;
-#pragma unroll
-        for (int g16 = 0; g16 < 4; ++g16) {
-          const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e], c2, -m_use));
-            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e + 1], c2, -m_use));
-            ps += x0 + x1;
-            w[e] = pack_bf16x2(x0, x1);
-          }
-          P[nb][g16] = as_bf16x8(w);
-        }
-        l_run[nb] = l_run[nb] * alpha + ps;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r0 + 2 * e], c2, -m_use));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r0 + 2 * e + 1], c2, -m_use));
+        ps += x0 + x1;
+        w[e] = pack_bf16x2(x0, x1);
       }
-
-    // O^T += V^T P^T
+      P[g16] = as_bf16x8(w);
+    }
+    l_run = l_run * alpha + ps;
+    // O^T += V^T P^T, V^T operands by transposed LDS reads
+    // V^T fragments, also read one product ahead
+    auto vfrag = [&](int n) { return lds_read_tr_pair(cV + vofs[n / 4] + (n % 4) * 16 * D, D); };
+    bf16x8 va = vfrag(0);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int g16 = 0; g16 < 4; ++g16) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            sVT + (db * 32 + col) * VSTR + 16 * g16 + 8 * half));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb][db] = mfma32(a, P[nb][g16], acc[nb][db]);
-      }
+    for (int n = 0; n < D / 8; ++n) {  // n = 4 db + g16
+      const bf16x8 cur = va;
+      if (n + 1 < D / 8) va = vfrag(n + 1);
+      acc[n / 4] = mfma32(cur, P[n % 4], acc[n / 4]);
     }
   };
-  // leading tiles wholly inside the past range need no mask
-  const int n_full = min(max(n_past / kKeyTile - pt0, 0), npt);
-  for (int t = 0; t < n_full; ++t) tile(t, std::false_type{});
-  for (int t = n_full; t < n_tiles; ++t) tile(t, std::true_type{});
+
+  // Tile t lives in stage t & 1.  Iteration t: wait for its loads (own, then
+  // everyone's via the barrier, which also retires all reads of tile t - 1),
+  // start the loads of tile t + 1 into the other stage and the index loads of
+  // tile t + 2, then compute tile t.
+  if (n_tiles > 0) {
+    rows_of(0);
+    issue(0, sK0, sV0);
+    if (n_tiles > 1) rows_of(1);
+  }
+  auto step = [&](int t, uint16_t* cK, uint16_t* cV, uint16_t* nK, uint16_t* nV) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's loads of tile t landed
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      issue(t + 1, nK, nV);
+      if (t + 2 < n_tiles) rows_of(t + 2);
+    }
+    if (wave_active) compute(t, cK, cV);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sK0, sV0, sK1, sV1);
+    if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
+  }
 
   // epilogue: lane (col, half) holds query col, d rows db*32 + 8*(r/4) + 4*half + r%4
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    const int r = row0 + (wave * NB + nb) * 32 + col;
-    if (r >= M) continue;
-    const int i = iq[nb], g = r - (r / G) * G;
+  {
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    const int r = row0 + wave * 32 + col;
+    if (r >= M) return;
+    const int i = iq, g = r - (r / G) * G;
     const size_t orow = (static_cast<size_t>(b) * p.nq + j * G + g) * bcp + i;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse2 = lt > 0.f ? m_run[nb] + log2f(lt) : -INFINITY;
+    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
     if (p.n_split == 1) {
       uint16_t* op = p.out + orow * D;
 #pragma unroll
@@ -336,8 +355,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * half;
           uint2 w;
-          w.x = pack_bf16x2(acc[nb][db][4 * r4] * inv, acc[nb][db][4 * r4 + 1] * inv);
-          w.y = pack_bf16x2(acc[nb][db][4 * r4 + 2] * inv, acc[nb][db][4 * r4 + 3] * inv);
+          w.x = pack_bf16x2(acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv);
+          w.y = pack_bf16x2(acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv);
           *reinterpret_cast<uint2*>(op + d0) = w;
         }
       if (p.lse && half == 0) p.lse[orow] = lse2 * kLn2;
@@ -349,8 +368,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * half;
-          f32x4 w = {acc[nb][db][4 * r4] * inv, acc[nb][db][4 * r4 + 1] * inv,
-                     acc[nb][db][4 * r4 + 2] * inv, acc[nb][db][4 * r4 + 3] * inv};
+          f32x4 w = {acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv,
+                     acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
           *reinterpret_cast<f32x4*>(op + d0) = w;
         }
       if (half == 0) p.part_lse[static_cast<size_t>(split) * rows_total + orow] = lse2;
@@ -474,9 +493,12 @@ Plan make_plan(int b, int nq, int nkv, int d, int bcp, int n_past_max) {
   return pl;
 }
 
-template <int D, int NB, int WAVES, int OCC>
+template <int D, int WAVES, int OCC>
 hipError_t run_bf16(const AttnParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NB, WAVES, OCC>), dim3(grid), dim3(64 * WAVES), 0, st, p);
+  if (p.idx)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, OCC, true>), dim3(grid), dim3(64 * WAVES), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, OCC, false>), dim3(grid), dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 
@@ -538,9 +560,9 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   }
   const int grid = pl.n_qtiles * c.b * c.nkv * pl.n_split;
   hipError_t e;
-  if (c.d == 128) e = run_bf16<128, 1, 4, 2>(p, grid, st);
-  else if (c.d == 64) e = run_bf16<64, 1, 4, 2>(p, grid, st);
-  else if (c.d == 256) e = run_bf16<256, 1, 4, 1>(p, grid, st);
+  if (c.d == 128) e = run_bf16<128, 4, 2>(p, grid, st);
+  else if (c.d == 64) e = run_bf16<64, 4, 2>(p, grid, st);
+  else if (c.d == 256) e = run_bf16<256, 4, 1>(p, grid, st);
   else return hipErrorInvalidValue;
   if (e != hipSuccess || pl.n_split == 1) return e;
   const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4)), cblock(256);
