@@ -231,7 +231,7 @@ def main():
     if not args.no_dense:
         dout = torch.empty_like(inputs[0]["q"])
         nws = qk.qk_workspace_bytes(shape, "dense_attn")
-        dws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        dws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
         for i in range(3):
             c = inputs[i % copies]
             qk.qk_dense_attn(shape, c["q"], c["k"], c["v"], dout, None, dws, nws)

@@ -39,7 +39,9 @@
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer past
  * return and allocates nothing.  Outputs must not alias inputs.  Scratch memory
- * comes from the caller as (ws, ws_bytes), sized by qk_workspace_bytes.
+ * comes from the caller as (ws, ws_bytes), sized by qk_workspace_bytes; its
+ * contents need no initialisation and are dead after the call.  Calls that use
+ * one workspace concurrently (different streams) race.
  *
  * Execution: every call validates its arguments on the host, enqueues its
  * kernels on `stream` and returns without synchronising.  The library holds no
@@ -82,7 +84,9 @@ typedef struct {
   int32_t d;        /* head dim: 64, 128 or 256                                  */
   int32_t bcp;      /* chunk queries, 1 .. 4096 (1 = decode)                     */
   int32_t t_past;   /* T, past positions scored, >= 0 (>= 1 for selection)        */
-  int32_t kv_cap;   /* rows per (sequence, KV head) in k and v, >= t_past + bcp  */
+  int32_t kv_cap;   /* rows per (sequence, KV head) in k and v, >= t_past + bcp;
+                       kv_cap * d * 4 must not exceed INT32_MAX (else
+                       QK_ERR_UNSUPPORTED)                                    */
   int32_t nq_keep;  /* NQ, kept queries per head, 1 .. min(bcp, 256)             */
   int32_t bsa;      /* BSA, kept keys per KV head, >= 1; values above T act as T */
   float scale;      /* softmax scale; 0 means 1/sqrt(d)                          */

@@ -205,7 +205,7 @@ def _ws(shape: Shape, op: str, device) -> tuple:
     n = qk_workspace_bytes(shape, op)
     if n == 0:
         return None, 0
-    return torch.empty(n, dtype=torch.uint8, device=device), n
+    return torch.zeros(n, dtype=torch.uint8, device=device), n
 
 
 class Pipeline:

@@ -27,6 +27,8 @@ qk_status check_shape(const qk_shape* s) {
   if (s->t_past < 0) return QK_ERR_SHAPE;
   if (static_cast<int64_t>(s->kv_cap) < static_cast<int64_t>(s->t_past) + s->bcp) return QK_ERR_SHAPE;
   if (!(s->scale >= 0.f) || isinf(s->scale)) return QK_ERR_SHAPE;
+  // one (sequence, KV head) block of the cache is addressed with 32-bit offsets
+  if (static_cast<int64_t>(s->kv_cap) * s->d * 4 > INT32_MAX) return QK_ERR_UNSUPPORTED;
   return QK_OK;
 }
 
@@ -205,6 +207,7 @@ qk_status qk_sparse_attn(const qk_shape* s, const void* q, const void* k_sel, co
       return QK_ERR_ALIGN;
   }
   if (ld_sel < (sel_len ? 1 : n_sel)) return QK_ERR_SHAPE;
+  if (static_cast<int64_t>(ld_sel) * s->d * 4 > INT32_MAX) return QK_ERR_UNSUPPORTED;
   return attn_common(s, q, k_sel, v_sel, ld_sel, nullptr, 0, sel_len, n_sel, k, v, out, lse, ws,
                      ws_bytes, QK_OP_SPARSE_ATTN, stream);
 }

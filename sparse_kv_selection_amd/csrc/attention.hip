@@ -10,12 +10,14 @@
 //   * GQA packing: the G query heads of one KV head are one matrix of G*bcp
 //     rows, row r = query position r / G of head r % G (position-major, so a
 //     row block spans few positions and causal chunk tiles can be skipped);
-//   * a workgroup of WAVES waves owns WAVES * NB * 32 rows and walks one split
-//     of the key range in tiles of 64 keys; tiles are fetched one ahead into
-//     registers with 16-byte loads (rows through the index list when the
-//     selection is not gathered), then stored to LDS: K row-major with a
-//     16-byte row pad, V transposed (d-major) with the keys of each 16-key
-//     group permuted so that one 16-byte LDS read yields a matrix-core operand;
+//   * a workgroup of WAVES waves owns WAVES * 32 rows and walks one split of
+//     the key range in tiles of 64 keys; each tile is copied global -> LDS by
+//     16-byte direct loads (rows through the index list when the selection is
+//     not gathered; index entries fetched one tile ahead), with the 16-byte
+//     chunks of each row XOR-swizzled so that the matrix-core reads spread
+//     over all banks; two LDS stages, so tile t + 1 streams in while tile t is
+//     computed; V stays row-major and its transposed operand comes from the
+//     LDS transpose read;
 //   * S^T = K Q^T: keys are the matrix rows, queries the columns, so every
 //     softmax statistic of a query lives in one lane pair (lane l and l ^ 32);
 //   * online softmax in base 2 with the scale folded into one multiply;
@@ -144,14 +146,14 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   // l writes chunk position l % CH of row r = ... + l / CH and so fetches the
   // global chunk (l % CH) ^ swz(r) of that key's row.
   int trow[IPW];     // tile row of each load of this lane
-  int kchunk[IPW];   // element offset of the fetched chunk, K
-  int vchunk[IPW];   // element offset of the fetched chunk, V
+  int kchunk[IPW];   // byte offset of the fetched chunk in its row, K
+  int vchunk[IPW];   // byte offset of the fetched chunk in its row, V
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * RPI + lane / CH;
     trow[i] = r;
-    kchunk[i] = 8 * ((lane % CH) ^ swz_k<D>(r));
-    vchunk[i] = 8 * ((lane % CH) ^ swz_v<D>(r));
+    kchunk[i] = 16 * ((lane % CH) ^ swz_k<D>(r));
+    vchunk[i] = 16 * ((lane % CH) ^ swz_v<D>(r));
   }
   // Key rows of a tile.  Keys past the end of the range are clamped onto a
   // valid row; they are masked to -inf, so their weight is exactly 0.  Index
@@ -176,11 +178,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     const int hi = past ? row_hi : bcp - 1;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const uint32_t ro = static_cast<uint32_t>(min(max(krow[i], 0), hi)) * D;
+      // one 32-bit byte offset from a wave-uniform base (scalar-base loads)
+      const uint32_t ro = static_cast<uint32_t>(min(max(krow[i], 0), hi)) * (2 * D);
       uint16_t* lk = dK + (wave * IPW + i) * 512;
       uint16_t* lv = dV + (wave * IPW + i) * 512;
-      lds_load16(kbase + ro + kchunk[i], lk);
-      lds_load16(vbase + ro + vchunk[i], lv);
+      lds_load16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kbase) +
+                                                   (ro + static_cast<uint32_t>(kchunk[i]))),
+                 lk);
+      lds_load16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vbase) +
+                                                   (ro + static_cast<uint32_t>(vchunk[i]))),
+                 lv);
     }
   };
 
@@ -266,21 +273,25 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) S[kb][r] = -INFINITY;
     }
+    // Lazy rescale: the reference maximum of a query only moves when a score
+    // exceeds it by more than kSlack (base 2), so probabilities stay below
+    // 2^kSlack and the accumulator is rescaled on few tiles; the softmax is
+    // unchanged (numerator and denominator share the reference).  Both lanes
+    // of a query (l and l ^ 32) take the same decision from the exchanged
+    // maxima, so their halves of the key sum share one reference, and the
+    // common case needs no exchange at all.
     float mx = S[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    // Lazy rescale: the running maximum only moves when the tile's maximum
-    // exceeds it by more than kSlack (base 2), so probabilities stay below
-    // 2^kSlack and the accumulator is rescaled on few tiles.  The result is
-    // the same softmax: numerator and denominator share the reference.
-    float alpha = 1.f;
+    mx *= c2;
     if (__any(mx > m_run + kSlack)) {
-      const float m_new = mx > m_run + kSlack ? mx : m_run;
-      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float mq = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = mq > m_run + kSlack ? mq : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
     }
@@ -302,16 +313,19 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
       }
       P[g16] = as_bf16x8(w);
     }
-    l_run = l_run * alpha + ps;
-    // O^T += V^T P^T, V^T operands by transposed LDS reads
-    // V^T fragments, also read one product ahead
-    auto vfrag = [&](int n) { return lds_read_tr_pair(cV + vofs[n / 4] + (n % 4) * 16 * D, D); };
+    l_run += ps;
+    // O^T += V^T P^T, the key groups in order so that the products of the
+    // first half can start while the second half's exponentials run; V^T
+    // operands come from transposed LDS reads, one product ahead
+    auto vfrag = [&](int n) {  // key group n / (D / 32), d block n % (D / 32)
+      return lds_read_tr_pair(cV + vofs[n % (D / 32)] + (n / (D / 32)) * 16 * D, D);
+    };
     bf16x8 va = vfrag(0);
 #pragma unroll
-    for (int n = 0; n < D / 8; ++n) {  // n = 4 db + g16
+    for (int n = 0; n < D / 8; ++n) {
       const bf16x8 cur = va;
       if (n + 1 < D / 8) va = vfrag(n + 1);
-      acc[n / 4] = mfma32(cur, P[n % 4], acc[n / 4]);
+      acc[n % (D / 32)] = mfma32(cur, P[n / (D / 32)], acc[n % (D / 32)]);
     }
   };
 

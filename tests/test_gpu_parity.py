@@ -150,7 +150,7 @@ def test_attention_on_oracle_selection(gpu, name, fused):
     out = torch.empty_like(g["q"])
     lse = torch.empty((s.b, s.nq, s.bcp), dtype=torch.float32, device=dev)
     nws = qk.qk_workspace_bytes(s, "sparse_attn")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
     if fused:
         qk.qk_sparse_attn_indexed(s, g["q"], g["k"], g["v"], kidx, n_sel, None, out, lse, ws, nws)
     else:
@@ -177,7 +177,7 @@ def test_dense_attention(gpu, name):
     out = torch.empty_like(g["q"])
     lse = torch.empty((s.b, s.nq, s.bcp), dtype=torch.float32, device=dev)
     nws = qk.qk_workspace_bytes(s, "dense_attn")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
     qk.qk_dense_attn(s, g["q"], g["k"], g["v"], out, lse, ws, nws)
     torch.cuda.synchronize()
     want_o, want_lse = oracle.dense_attention(np64(case["q"]), np64(case["k"]), np64(case["v"]),
@@ -231,7 +231,7 @@ def test_sparse_equals_dense_at_full_budget(gpu):
     pipe(g["q"], g["k"], g["v"])
     out = torch.empty_like(g["q"])
     nws = qk.qk_workspace_bytes(s, "dense_attn")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=_dev())
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=_dev())
     qk.qk_dense_attn(s, g["q"], g["k"], g["v"], out, None, ws, nws)
     torch.cuda.synchronize()
     assert np.array_equal(npi(pipe.idx)[0, 0], np.arange(s.t_past))
@@ -277,7 +277,7 @@ def test_round_select_and_attention(gpu, name):
     s2 = qk.shape_of(spec, bsa=ld)
     out = torch.empty_like(g["q"])
     nws = qk.qk_workspace_bytes(s2, "sparse_attn")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
     qk.qk_sparse_attn_indexed(s2, g["q"], g["k"], g["v"], torch.from_numpy(kidx).to(dev), ld,
                               torch.from_numpy(lens).to(dev), out, None, ws, nws)
     torch.cuda.synchronize()
@@ -351,7 +351,7 @@ def test_zero_keys_and_empty_past(gpu):
     s0.kv_cap = kk.shape[2]
     out = torch.empty_like(g["q"])
     nws = qk.qk_workspace_bytes(s0, "dense_attn")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=_dev())
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=_dev())
     qk.qk_dense_attn(s0, g["q"], kk, vv, out, None, ws, nws)
     torch.cuda.synchronize()
     want, _ = oracle.dense_attention(np64(case["q"]), np64(case["k"][:, :, 300:]),
@@ -370,3 +370,30 @@ def test_deterministic(gpu):
     torch.cuda.synchronize()
     for n in ("q_idx", "q_group", "s_agg", "idx", "out", "lse"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+
+
+def test_workspace_reuse_across_calls(gpu):
+    """One workspace serves consecutive key-split attention calls of different
+    sizes (a large call, a smaller one, the large one again): identical
+    outputs for identical calls, each matching the oracle."""
+    qk = gpu
+    spec = W.spec("llama3b_32k", t_past=4096, bsa=1024, bcp=128)
+    case = W.make_case(spec, 33)
+    g = {n: case[n].to(_dev()) for n in ("q", "k", "v")}
+    s = qk.shape_of(spec)
+    nws = qk.qk_workspace_bytes(s, "dense_attn")
+    assert nws > 0, "this shape is meant to use key splits"
+    ws = torch.full((nws,), 0x7f, dtype=torch.uint8, device=_dev())  # contents are don't-care
+    outs = []
+    small = qk.Shape(s.b, s.nq, s.nkv, s.d, s.bcp, 1024, s.kv_cap, s.nq_keep, s.bsa)
+    for shp in (s, small, s):
+        out = torch.empty_like(g["q"])
+        lse = torch.empty(s.b, s.nq, s.bcp, dtype=torch.float32, device=_dev())
+        qk.qk_dense_attn(shp, g["q"], g["k"], g["v"], out, lse, ws, nws)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    want, _ = oracle.dense_attention(np64(case["q"]), np64(case["k"]), np64(case["v"]), 4096)
+    assert max_abs(outs[0][0], want) <= ATTN_TOL["bf16"]
+    want_s, _ = oracle.dense_attention(np64(case["q"]), np64(case["k"]), np64(case["v"]), 1024)
+    assert max_abs(outs[1][0], want_s) <= ATTN_TOL["bf16"]
