@@ -7,7 +7,9 @@
 //
 // The pass is bound by HBM: every past key (d bf16) is read once and 4 bytes
 // are written per key.  bf16 kernel (d = 64/128/256):
-//   * every wave streams its own run of 32-key blocks -- no LDS, no barriers.
+//   * every wave streams its own share of 32-key blocks -- no LDS, no
+//     barriers; the waves of one KV head interleave their blocks so that the
+//     concurrent streams spread over the HBM channels.
 //     Lane (c, h) loads key c's d-slots [16s + 8h, 16s + 8h + 8) as one
 //     16-byte load per step s, which is exactly the matrix-core operand
 //     layout (keys as the 32 columns of a 32x32x16 bf16 tile); every load
@@ -20,7 +22,8 @@
 //   * the fp32 group queries are split into bf16 high and low parts and both
 //     are multiplied (error about 2^-16 relative instead of 2^-8); the matrix
 //     cores stay far below their roofline either way;
-//   * |k|^2 is summed in fp32 from the same registers.
+//   * |k|^2 is summed in fp32 from the same registers (packed bf16 dot
+//     products).
 // Query rows beyond NQ in the last 32-row block repeat query 0, which leaves
 // the max unchanged.
 #include "qk_device.h"
@@ -42,9 +45,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
   const int waves_per_bj = (blocks_per_bj + blocks_per_wave - 1) / blocks_per_wave;
   const int gw = blockIdx.x * kScoreWaves + wave;
   const int bj = gw / waves_per_bj;
-  const int blk0 = (gw % waves_per_bj) * blocks_per_wave;
-  const int blk1 = min(blk0 + blocks_per_wave, blocks_per_bj);
-  if (bj >= bnkv || blk0 >= blk1) return;
+  // Wave wi of this (b, KV head) takes blocks wi, wi + W, wi + 2W, ... (W the
+  // waves per head): at any moment the head's waves read neighbouring blocks,
+  // so the concurrent streams spread over the HBM channels instead of every
+  // wave sitting at the same offset of an equally aligned private run.
+  const int wi = gw % waves_per_bj;
+  const int nblk = wi < blocks_per_bj ? (blocks_per_bj - wi + waves_per_bj - 1) / waves_per_bj : 0;
+  if (bj >= bnkv || nblk == 0) return;
+  auto block_of = [&](int m) { return wi + m * waves_per_bj; };
 
   const uint16_t* kb = k + static_cast<size_t>(bj) * kv_cap * D + 8 * half;
   float* out = s_agg + static_cast<size_t>(bj) * t_past;
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
   // first blocks in flight before the query fragments are built
 #pragma unroll
   for (int i = 0; i < STAGES - 1; ++i)
-    if (blk0 + i < blk1) load_block(blk0 + i, buf[i]);
+    if (i < nblk) load_block(block_of(i), buf[i]);
 
   bf16x8 qhi[NQB][NS], qlo[NQB][NS];
   {
@@ -94,12 +102,19 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
     float n2 = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float a = bf16lo(w[s][p]), bb = bf16hi(w[s][p]);
-        n2 += a * a + bb * bb;
-      }
       const bf16x8 kf = as_bf16x8(w[s]);
+      // |k|^2: one packed bf16 dot product per pair (the products are exact in
+      // fp32, accumulation in fp32).  The pairs are taken from the bf16x8
+      // operand by shuffles: a bit cast of a single 32-bit vector element was
+      // observed to read the wrong register at -O3.
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 0, 1),
+                                           __builtin_shufflevector(kf, kf, 0, 1), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 2, 3),
+                                           __builtin_shufflevector(kf, kf, 2, 3), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 4, 5),
+                                           __builtin_shufflevector(kf, kf, 4, 5), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 6, 7),
+                                           __builtin_shufflevector(kf, kf, 6, 7), n2, false);
 #pragma unroll
       for (int mb = 0; mb < NQB; ++mb) {
         acc[mb] = mfma32(qhi[mb][s], kf, acc[mb]);
@@ -114,18 +129,19 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
     m = fmaxf(m, __shfl_xor(m, 32));
     n2 += __shfl_xor(n2, 32);
     const int key = blk * kBlock + col;
-    if (half == 0 && key < t_past) out[key] = m / fmaxf(sqrtf(n2), kEps);
+    // m / max(|k|, eps) as m * rsqrt(max(|k|^2, eps^2))
+    if (half == 0 && key < t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
   };
 
-  // unrolled ring: block blk lives in buf[(blk - blk0) % STAGES]
-  for (int base = blk0; base < blk1; base += STAGES) {
+  // unrolled ring: this wave's m-th block lives in buf[m % STAGES]
+  for (int base = 0; base < nblk; base += STAGES) {
 #pragma unroll
     for (int i = 0; i < STAGES; ++i) {
-      const int blk = base + i;
-      if (blk >= blk1) break;
-      const int nxt = blk + STAGES - 1;
-      if (nxt < blk1) load_block(nxt, buf[(i + STAGES - 1) % STAGES]);
-      score_block(blk, buf[i]);
+      const int m = base + i;
+      if (m >= nblk) break;
+      const int nxt = m + STAGES - 1;
+      if (nxt < nblk) load_block(block_of(nxt), buf[(i + STAGES - 1) % STAGES]);
+      score_block(block_of(m), buf[i]);
     }
   }
 }
@@ -159,9 +175,11 @@ void launch_bf16(const float* qg, const uint16_t* k, float* s, int bnkv, int t_p
                  int nq_keep, hipStream_t st) {
   constexpr int STAGES = 4;
   const int blocks_per_bj = (t_past + kBlock - 1) / kBlock;
-  // about one resident wave per SIMD, each streaming a run of blocks
+  // about as many waves as are resident (two per SIMD where the registers
+  // allow, else one), each streaming its share of blocks
+  constexpr long long kResident = (D == 256 || NQB > 1) ? 1024 : 2048;
   const long long total = static_cast<long long>(blocks_per_bj) * bnkv;
-  long long bpw = (total + 1023) / 1024;
+  long long bpw = (total + kResident - 1) / kResident;
   if (bpw < 2) bpw = 2;
   if (bpw > blocks_per_bj) bpw = blocks_per_bj;
   const long long waves = ((blocks_per_bj + bpw - 1) / bpw) * static_cast<long long>(bnkv);

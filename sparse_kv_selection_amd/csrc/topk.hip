@@ -80,31 +80,37 @@ __device__ int block_excl_scan(int v, int* wsum, int* total) {
   return off + x - v;
 }
 
-// Wave 0: the bin b of counts h[0..nb) (nb a multiple of 64) with
-// count(bins > b) < need <= count(bins >= b); writes (*bin, *above).
-__device__ void wave_crossing(const int* h, int nb, int need, int* bin, int* above) {
+// Wave 0 only: the bin b of counts h[0..64 * PER) with
+// count(bins > b) < need <= count(bins >= b); writes (*bin, *above) from the
+// lane that holds it.  Each lane keeps its PER bins in registers, so the search
+// is one batch of LDS reads, one wave scan and a register walk.
+template <int PER>
+__device__ void wave_crossing(const int* h, int need, int* bin, int* above) {
   const int lane = threadIdx.x & 63;
-  const int per = nb / 64;
-  const int top = nb - 1 - lane * per;
+  const int top = 64 * PER - 1 - lane * PER;  // lane 0 holds the highest bins
+  int c[PER];
   int sum = 0;
-  for (int q = 0; q < per; ++q) sum += h[top - q];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    c[q] = h[top - q];
+    sum += c[q];
+  }
   int incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  int ex = incl - sum;
+  const int ex = incl - sum;
   if (ex < need && need <= incl) {
-    for (int q = 0; q < per; ++q) {
-      const int c = h[top - q];
-      if (need <= ex + c) {
-        *bin = top - q;
-        *above = ex;
-        break;
-      }
-      ex += c;
+    int b = top, a = ex;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (a + c[q] >= need) { b = top - q; break; }
+      a += c[q];
     }
+    *bin = b;
+    *above = a;
   }
 }
 
@@ -148,7 +154,7 @@ __device__ void exact_threshold(TopkShared& sh, int need, VisitBin visit_bin) {
       visit_bin([&](float x) { count(fkey(x)); });
     }
     __syncthreads();
-    if (wave == 0) wave_crossing(sh.hist, 256, need, &sh.bin, &sh.above);
+    if (wave == 0) wave_crossing<4>(sh.hist, need, &sh.bin, &sh.above);
     __syncthreads();
     need -= sh.above;
     prefix |= static_cast<uint32_t>(min(max(sh.bin, 0), 255)) << shift;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
     else bins[e >> 1] = static_cast<uint32_t>(b);
   }
   __syncthreads();
-  if (wave == 0) wave_crossing(sh.hist, kBins, k, &sh.bin, &sh.above);
+  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin, &sh.above);
   __syncthreads();
   const uint32_t B = static_cast<uint32_t>(min(max(sh.bin, 0), kBins - 1));
   const int need0 = k - sh.above;
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(const float* 
     for (int e = 0; e < kRun; ++e) atomicAdd(&sh.hist[bin_of(x[e])], 1);
   });
   __syncthreads();
-  if (wave == 0) wave_crossing(sh.hist, kBins, k, &sh.bin, &sh.above);
+  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin, &sh.above);
   __syncthreads();
   const uint32_t B = static_cast<uint32_t>(min(max(sh.bin, 0), kBins - 1));
   const int need0 = k - sh.above;

@@ -325,6 +325,23 @@ def test_topk_edge_cases(gpu):
     _topk_check(qk, rng.standard_normal((3, 1)).astype(np.float32), 1)
     _topk_check(qk, rng.standard_normal((3, 333)).astype(np.float32), 1, ld_idx=5)
     _topk_check(qk, rng.uniform(-1, 1, (2, 131072)).astype(np.float32), 16384)
+    # rows whose sampled elements (index blocks 4j * 1024 .. + 1023 of each
+    # 32K tile) look nothing like the rest: the sample's band misses and the
+    # full histogram takes over
+    x = rng.standard_normal((3, 32768)).astype(np.float32)
+    blk = (np.arange(32768) // 1024) % 4 == 0
+    x[:, blk] += 5.0
+    _topk_check(qk, x, 8192)
+    _topk_check(qk, x, 9000)
+    x = rng.standard_normal((2, 20000)).astype(np.float32)  # partial tile
+    x[:, ((np.arange(20000) // 1024) % 4) == 0] -= 4.0
+    _topk_check(qk, x, 5000)
+    # skewed, ragged and extreme k
+    _topk_check(qk, rng.exponential(1.0, (3, 32768)).astype(np.float32), 8192)
+    _topk_check(qk, rng.standard_normal((2, 12345)).astype(np.float32), 1)
+    _topk_check(qk, rng.standard_normal((2, 12345)).astype(np.float32), 12344)
+    _topk_check(qk, rng.standard_normal((2, 65536 + 77)).astype(np.float32), 3333)
+    _topk_check(qk, np.round(rng.standard_normal((2, 32768)), 2).astype(np.float32), 8192)  # ties
     # a dense cluster at the boundary (more than fits in LDS): global fallback
     x = rng.uniform(0, 1e-6, (2, 40000)).astype(np.float32) + 0.5
     x[:, :100] = 2.0
