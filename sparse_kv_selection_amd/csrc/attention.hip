@@ -23,8 +23,8 @@
 //   * online softmax in base 2 with the scale folded into one multiply;
 //     probabilities are rounded to bf16 and O^T = V^T P^T accumulates in fp32,
 //     again one query per lane column, so the rescale is a per-lane multiply;
-//   * key splits write normalised fp32 partials and a log-sum-exp; a combine
-//     kernel merges them.
+//   * key splits write normalised partials (fp16, scaled per row) and a
+//     log-sum-exp; a combine kernel merges them.
 // fp32 kernel: one thread per query row, fp32 throughout (small workloads).
 #include <math.h>
 
@@ -50,8 +50,8 @@ struct AttnParams {
   int kv_cap, t_past;
   uint16_t* out;
   float* lse;
-  float* part_o;
-  float* part_lse;
+  uint32_t* part_o;   // split partials, fp16 pairs scaled to [-1, 1]
+  float2* part_ls;    // per (split, row): (base-2 log-sum-exp, scale)
   int b, nq, nkv, G, bcp;
   int n_qtiles, n_split;
   float scale_log2;
@@ -375,64 +375,84 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         }
       if (p.lse && half == 0) p.lse[orow] = lse2 * kLn2;
     } else {
+      // normalised partial, scaled by its row's largest magnitude M so that
+      // fp16 keeps a relative precision of 2^-11 of M whatever the range of V;
+      // M and the log-sum-exp stay fp32
       const size_t rows_total = static_cast<size_t>(p.b) * p.nq * bcp;
-      float* op = p.part_o + (static_cast<size_t>(split) * rows_total + orow) * D;
+      float mag = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mag = fmaxf(mag, fabsf(acc[db][r]));
+      mag = fmaxf(mag, __shfl_xor(mag, 32)) * inv;
+      const float sc = mag > 0.f ? inv / mag : 0.f;
+      uint32_t* op = p.part_o + (static_cast<size_t>(split) * rows_total + orow) * (D / 2);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * half;
-          f32x4 w = {acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv,
-                     acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + d0) = w;
+          uint2 w;
+          w.x = pack_f16x2(acc[db][4 * r4] * sc, acc[db][4 * r4 + 1] * sc);
+          w.y = pack_f16x2(acc[db][4 * r4 + 2] * sc, acc[db][4 * r4 + 3] * sc);
+          *reinterpret_cast<uint2*>(op + d0 / 2) = w;
         }
-      if (half == 0) p.part_lse[static_cast<size_t>(split) * rows_total + orow] = lse2;
+      if (half == 0) p.part_ls[static_cast<size_t>(split) * rows_total + orow] = float2{lse2, mag};
     }
   }
 }
 
 // Merge key-split partials, one wave per output row:
-//   O = sum_s w_s O_s / sum_s w_s,  w_s = 2^(lse_s - max_s lse_s)
-// Lane s < n_split (<= 64) holds split s's log-sum-exp; every lane then loads
-// its d-slots of all splits at once.
+//   O = sum_s w_s M_s P_s / sum_s w_s,  w_s = 2^(lse_s - max_s lse_s),
+// P_s the fp16 partial scaled by 1 / M_s.  Lane s < n_split (<= 64) holds split
+// s's (lse, M); every lane then loads its d-slots of all splits at once.
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const uint32_t* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ls,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse, int n_split,
                                                            long long rows) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 128;  // fp16 pairs per lane
   const int lane = threadIdx.x & 63;
   const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float ls = lane < n_split ? part_lse[lane * rows + row] : -INFINITY;
-  const float mx = wave_max(ls);
-  const float w = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+  const float2 lm = lane < n_split ? part_ls[lane * rows + row] : float2{-INFINITY, 0.f};
+  const float mx = wave_max(lm.x);
+  const float w = (lm.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lm.x - mx);
   const float wsum = wave_sum(w);
-  float acc[PER];
+  const float f = w * lm.y;  // weight of the scaled partial
+  float acc[2 * (PER > 0 ? PER : 1)];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 2 * (PER > 0 ? PER : 1); ++e) acc[e] = 0.f;
   constexpr int kBatch = 16;
   for (int s0 = 0; s0 < n_split; s0 += kBatch) {
-    float x[kBatch][PER];
+    uint32_t x[kBatch][PER > 0 ? PER : 1];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sidx = min(s0 + u, n_split - 1);
-      const float* src = part_o + (sidx * rows + row) * D + lane;
+      const uint32_t* src = part_o + (sidx * rows + row) * (D / 2);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) x[u][e] = src[64 * e];
+      for (int e = 0; e < (PER > 0 ? PER : 1); ++e)
+        x[u][e] = (PER > 0 || lane < D / 2) ? src[lane + 64 * e] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float wu = s0 + u < n_split ? __shfl(w, s0 + u) : 0.f;
+      const float fu = s0 + u < n_split ? __shfl(f, s0 + u) : 0.f;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += wu * x[u][e];
+      for (int e = 0; e < (PER > 0 ? PER : 1); ++e) {
+        const f32x2 v = unpack_f16x2(x[u][e]);
+        acc[2 * e] += fu * v[0];
+        acc[2 * e + 1] += fu * v[1];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* op = out + row * D + lane;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) op[64 * e] = f32_to_bf16(acc[e] * inv);
+  for (int e = 0; e < (PER > 0 ? PER : 1); ++e) {
+    const int d = 2 * (lane + 64 * e);
+    if (PER > 0 || lane < D / 2)
+      *reinterpret_cast<uint32_t*>(out + row * D + d) = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  }
   if (lse && lane == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
@@ -523,7 +543,8 @@ size_t attn_workspace_bytes(bool bf16, int b, int nq, int nkv, int d, int bcp, i
   const Plan pl = make_plan(b, nq, nkv, d, bcp, n_past_max);
   if (pl.n_split <= 1) return 0;
   const size_t rows = static_cast<size_t>(b) * nq * bcp;
-  return static_cast<size_t>(pl.n_split) * rows * (d + 1) * sizeof(float);
+  // fp16 partial outputs + (log-sum-exp, scale) per split and row
+  return static_cast<size_t>(pl.n_split) * rows * (d * 2 + sizeof(float2));
 }
 
 hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
@@ -569,8 +590,8 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   p.scale_log2 = scale * kLog2e;
   const size_t rows = static_cast<size_t>(c.b) * c.nq * c.bcp;
   if (pl.n_split > 1) {
-    p.part_o = static_cast<float*>(c.ws);
-    p.part_lse = p.part_o + static_cast<size_t>(pl.n_split) * rows * c.d;
+    p.part_o = static_cast<uint32_t*>(c.ws);
+    p.part_ls = reinterpret_cast<float2*>(p.part_o + static_cast<size_t>(pl.n_split) * rows * c.d / 2);
   }
   const int grid = pl.n_qtiles * c.b * c.nkv * pl.n_split;
   hipError_t e;
@@ -581,13 +602,13 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   if (e != hipSuccess || pl.n_split == 1) return e;
   const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4)), cblock(256);
   if (c.d == 128)
-    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, st, p.part_o, p.part_ls,
                        static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
   else if (c.d == 64)
-    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, st, p.part_o, p.part_ls,
                        static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
   else
-    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, cblock, 0, st, p.part_o, p.part_lse,
+    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, cblock, 0, st, p.part_o, p.part_ls,
                        static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
   return hipGetLastError();
 }

@@ -36,6 +36,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed fp16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+// packed fp16 pair -> two fp32 (exact)
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ __forceinline__ static float load(const float* p) { return *p; }

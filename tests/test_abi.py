@@ -141,11 +141,12 @@ def test_attention_rejects():
 
 
 def test_workspace_sizes():
-    # split-key partials: n_split * rows * (d + 1) floats, 0 when one split suffices
+    # split-key partials: per split and row, d fp16 values + (lse, scale) fp32;
+    # 0 when one split suffices
     s = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192)
     n = qk.qk_workspace_bytes(s, "sparse_attn")
     rows = 1 * 24 * 256
-    assert n > 0 and n % (rows * 129 * 4) == 0
+    assert n > 0 and n % (rows * (128 * 2 + 8)) == 0
     assert qk.qk_workspace_bytes(s, "qsel") == 0
     assert qk.qk_workspace_bytes(qk.Shape(1, 4, 2, 64, 64, 1024, 1088, 32, 256, dtype=qk.QK_F32),
                                  "sparse_attn") == 0
