@@ -111,18 +111,28 @@ __device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* ou
   }
 }
 
-// Longer chunks (no wave sort): rank of every position by counting the
-// scores that beat it (larger, or equal at a lower position), NT threads.
+// Top-NQ positions by rank: the rank of position i is the number of scores
+// that beat it (larger, or equal at a lower position), so ranks are unique and
+// order the kept queries by decreasing SQ, ties to the lower position.  TPP
+// consecutive threads share one position, each counting one segment of the
+// scores (from LDS, broadcast reads), then sum by shuffles.
 template <int NT>
 __device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_t* out) {
-  for (int i = threadIdx.x; i < bcp; i += NT) {
-    const float s = sq[i];
+  int tpp = 1;
+  while (tpp < 16 && tpp * 2 * bcp <= NT) tpp *= 2;
+  const int part = threadIdx.x & (tpp - 1);
+  const int slots = NT / tpp;
+  const int seg = (bcp + tpp - 1) / tpp;
+  const int j0 = part * seg, j1 = min(j0 + seg, bcp);
+  for (int i = threadIdx.x / tpp; i < bcp; i += slots) {
+    const float sc = sq[i];
     int rank = 0;
-    for (int i2 = 0; i2 < bcp; ++i2) {
-      const float s2 = sq[i2];
-      rank += (s2 > s) | ((s2 == s) & (i2 < i));
+    for (int j = j0; j < j1; ++j) {
+      const float s2 = sq[j];
+      rank += (s2 > sc) | ((s2 == sc) & (j < i));
     }
-    if (rank < nq_keep) out[rank] = i;
+    for (int o = 1; o < tpp; o <<= 1) rank += __shfl_xor(rank, o);
+    if (part == 0 && rank < nq_keep) out[rank] = i;
   }
 }
 
@@ -295,31 +305,27 @@ void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bc
   const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
   const dim3 grid(b * nq), block(NT);
   const T* qq = static_cast<const T*>(q);
-#define QK_HEAD(EE) \
-  hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, EE>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep)
-  if (bcp <= 64) QK_HEAD(1);
-  else if (bcp <= 128) QK_HEAD(2);
-  else if (bcp <= 256) QK_HEAD(4);
-  else if (bcp <= 512) QK_HEAD(8);
-  else if (bcp <= 1024) QK_HEAD(16);
-  else QK_HEAD(0);
-#undef QK_HEAD
+  // up to 64 positions: one-wave sort; beyond: rank counting over the block
+  if (bcp <= 64)
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  else
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
 }
 
 template <typename T, int D>
 hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, int nq, int nkv,
                int bcp, int nq_keep, hipStream_t st) {
   constexpr int CH = D / 8;
-  constexpr bool kBf16 = sizeof(T) == 2;
   if (bcp * CH <= 64) {
     launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, st);   // decode-sized chunks
+  } else if (bcp * CH <= 256) {
+    launch_head<T, D, 256, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, st);  // short chunks
   } else {
-    constexpr int NRL = 256 / CH;
+    constexpr int NRL = 1024 / CH;
     const int rpt = (bcp + NRL - 1) / NRL;
-    if (rpt <= 4) launch_head<T, D, 256, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
-    else if (rpt <= 16) launch_head<T, D, 256, 16>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
-    else if (kBf16 && rpt <= 32) launch_head<T, D, 256, (kBf16 ? 32 : 16)>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
-    else launch_head<T, D, 256, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    if (rpt <= 4) launch_head<T, D, 1024, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
   }
   hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
                      static_cast<const T*>(q), q_idx, q_group, nq, nkv, bcp, nq_keep);
