@@ -111,28 +111,43 @@ __device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* ou
   }
 }
 
-// Top-NQ positions by rank: the rank of position i is the number of scores
-// that beat it (larger, or equal at a lower position), so ranks are unique and
-// order the kept queries by decreasing SQ, ties to the lower position.  TPP
-// consecutive threads share one position, each counting one segment of the
-// scores (from LDS, broadcast reads), then sum by shuffles.
-template <int NT>
+// Top-NQ positions by rank.  With key(i) = (order-preserving SQ key << 32) |
+// ~i, the rank of position i is the number of keys larger than key(i) (larger
+// score, or equal score at a lower position): unique ranks that order the kept
+// queries by decreasing SQ, ties to the lower position.  16 consecutive
+// threads share a position; thread p of the group caches the keys of segment p
+// in registers (SEGMAX >= bcp / 16; 0: read from LDS instead), so every
+// comparison is one 64-bit compare,
+// and the 16 partial counts meet by shuffles.
+template <int NT, int SEGMAX>
 __device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_t* out) {
-  int tpp = 1;
-  while (tpp < 16 && tpp * 2 * bcp <= NT) tpp *= 2;
-  const int part = threadIdx.x & (tpp - 1);
-  const int slots = NT / tpp;
-  const int seg = (bcp + tpp - 1) / tpp;
-  const int j0 = part * seg, j1 = min(j0 + seg, bcp);
-  for (int i = threadIdx.x / tpp; i < bcp; i += slots) {
-    const float sc = sq[i];
+  constexpr int TPP = 16;
+  constexpr int SLOTS = NT / TPP;
+  const int part = threadIdx.x % TPP, slot = threadIdx.x / TPP;
+  const int seg = (bcp + TPP - 1) / TPP;
+  auto key = [&](int i) {
+    return (static_cast<uint64_t>(okey(sq[i])) << 32) | static_cast<uint32_t>(~i);
+  };
+  // SEGMAX == 0 (long chunks): the keys are read from LDS for every comparison
+  uint64_t kc[SEGMAX > 0 ? SEGMAX : 1];
+#pragma unroll
+  for (int e = 0; e < SEGMAX; ++e) {
+    const int j = part * seg + e;
+    kc[e] = (e < seg && j < bcp) ? key(j) : 0ull;  // 0 is below every real key
+  }
+  for (int i0 = 0; i0 < bcp; i0 += SLOTS) {  // uniform trip count (shuffles below)
+    const int i = i0 + slot;
+    const uint64_t ki = key(min(i, bcp - 1));
     int rank = 0;
-    for (int j = j0; j < j1; ++j) {
-      const float s2 = sq[j];
-      rank += (s2 > sc) | ((s2 == sc) & (j < i));
+    if constexpr (SEGMAX > 0) {
+#pragma unroll
+      for (int e = 0; e < SEGMAX; ++e) rank += kc[e] > ki;
+    } else {
+      for (int j = part * seg; j < min(part * seg + seg, bcp); ++j) rank += key(j) > ki;
     }
-    for (int o = 1; o < tpp; o <<= 1) rank += __shfl_xor(rank, o);
-    if (part == 0 && rank < nq_keep) out[rank] = i;
+#pragma unroll
+    for (int o = 1; o < TPP; o <<= 1) rank += __shfl_xor(rank, o);
+    if (part == 0 && i < bcp && rank < nq_keep) out[rank] = i;
   }
 }
 
@@ -140,7 +155,7 @@ __device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_
 // owns the 8-element chunk c of rows r, r + NT / CH, ...; RPT > 0: all of
 // them held in registers (one memory trip); RPT == 0: two passes over memory.
 // E > 0: wave 0 sorts 64 * E >= bcp keys; E == 0: rank count instead.
-template <typename T, int D, int NT, int RPT, int E>
+template <typename T, int D, int NT, int RPT, int E, int SEGMAX>
 __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
                                                        int32_t* __restrict__ q_idx,
                                                        float* __restrict__ sq_out, int bcp,
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   if constexpr (E > 0) {
     if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out);
   } else {
-    top_positions_rank<NT>(sq, bcp, nq_keep, out);
+    top_positions_rank<NT, SEGMAX>(sq, bcp, nq_keep, out);
   }
 }
 
@@ -306,10 +321,15 @@ void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bc
   const dim3 grid(b * nq), block(NT);
   const T* qq = static_cast<const T*>(q);
   // up to 64 positions: one-wave sort; beyond: rank counting over the block
+  // with bcp / 16 keys cached per thread
   if (bcp <= 64)
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  else if (bcp <= 256)
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 16>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  else if (bcp <= 512)
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 32>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
   else
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
 }
 
 template <typename T, int D>

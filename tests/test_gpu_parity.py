@@ -27,6 +27,8 @@ CASES = {
     "d64_nq40": ("llama3b_32k", dict(d=64, nq=8, nkv=2, t_past=2000, bcp=100, nq_keep=40, bsa=500), 7),
     "g1_all_keys": ("llama3b_32k", dict(nq=4, nkv=4, t_past=700, bcp=33, nq_keep=33, bsa=700), 8),
     "f32_d128": ("tiny_f32", dict(d=128, t_past=777, bcp=45, nq_keep=9, bsa=300), 9),
+    "long_chunk": ("llama3b_32k", dict(nq=6, nkv=2, t_past=1500, bcp=700, nq_keep=44, bsa=400), 10),
+    "chunk_300": ("llama3b_32k", dict(nq=4, nkv=2, t_past=900, bcp=300, nq_keep=37, bsa=200), 11),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
@@ -96,6 +98,24 @@ def test_qsel(gpu, name):
         rows = [qn[b, j * G + gg, gi[b, j * G + gg, n]] for gg in range(G)]
         want = np.mean([r / np.linalg.norm(r) for r in rows], axis=0)
         assert np.abs(gq[b, j, n] - want).max() <= 1e-5
+
+
+@pytest.mark.parametrize("bcp", [48, 200, 256, 300, 512, 700])
+def test_qsel_ties_keep_lower_positions(gpu, bcp):
+    """Every chunk query of a head equal (SQ all equal): the kept queries are
+    the first NQ positions in order, whatever the selection path."""
+    qk = gpu
+    spec = W.spec("llama3b_32k", nq=4, nkv=2, t_past=64, bcp=bcp, nq_keep=min(32, bcp), bsa=16)
+    s = qk.shape_of(spec)
+    g = torch.Generator().manual_seed(5)
+    row = torch.randn(s.b, s.nq, 1, s.d, generator=g).to(torch.bfloat16)
+    q = row.expand(s.b, s.nq, bcp, s.d).contiguous().to(_dev())
+    q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=torch.int32, device=_dev())
+    qg = torch.empty((s.b, s.nkv, s.nq_keep, s.d), dtype=torch.float32, device=_dev())
+    qk.qk_qsel(s, q, q_idx, None, qg)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(np.arange(s.nq_keep), (s.b, s.nq, s.nq_keep))
+    assert np.array_equal(npi(q_idx), want)
 
 
 # --------------------------------------------------------------------------
