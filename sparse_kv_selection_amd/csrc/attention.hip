@@ -10,7 +10,7 @@
 //   * GQA packing: the G query heads of one KV head are one matrix of G*bcp
 //     rows, row r = query position r / G of head r % G (position-major, so a
 //     row block spans few positions and causal chunk tiles can be skipped);
-//   * a workgroup of WAVES waves owns WAVES * 32 rows and walks one split of
+//   * a workgroup of WAVES waves owns WAVES * NB * 32 rows and walks one split of
 //     the key range in tiles of 64 keys; each tile is copied global -> LDS by
 //     16-byte direct loads (rows through the index list when the selection is
 //     not gathered; index entries fetched one tile ahead), with the 16-byte
@@ -89,9 +89,9 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
-template <int D, int WAVES, int OCC, bool IDX>
+template <int D, int NB, int WAVES, int OCC, bool IDX>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p) {
-  constexpr int ROWS = WAVES * 32;
+  constexpr int ROWS = WAVES * NB * 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 64 / CH;                // tile rows per wave-wide 16-byte load
   constexpr int IPW = kKeyTile / (RPI * WAVES);  // such loads per wave per matrix
@@ -191,21 +191,24 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     }
   };
 
-  // query fragments: lane (col, half) holds row col, d slots 16s + 8half + [0,8)
-  bf16x8 qf[D / 16];
-  int iq;
-  {
-    const int r = row0 + wave * 32 + col;
+  // query fragments: lane (col, half) holds row col of block nb, d slots
+  // 16s + 8half + [0,8); a wave owns NB independent blocks of 32 rows, whose
+  // softmax and products the compiler can interleave
+  bf16x8 qf[NB][D / 16];
+  int iq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = row0 + (wave * NB + nb) * 32 + col;
     const bool valid = r < M;
     const int i = r / G, g = r - (r / G) * G;
-    iq = i;
+    iq[nb] = i;
     const uint16_t* qp = p.q + ((static_cast<size_t>(b) * p.nq + j * G + g) * bcp + i) * D;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qf[s] = valid ? as_bf16x8(ld16(qp + 16 * s + 8 * half)) : bf16x8{};
+      qf[nb][s] = valid ? as_bf16x8(ld16(qp + 16 * s + 8 * half)) : bf16x8{};
   }
   // a wave whose rows are all padding only helps with the tile loads
-  const bool wave_active = row0 + wave * 32 < M;
+  const bool wave_active = row0 + wave * NB * 32 < M;
 
   // LDS read offsets (elements).  K: lane (col, half), step s reads row
   // kb*32 + col, chunk 2s + half -> position (2s) ^ fk with fk = half ^ swz.
@@ -232,24 +235,34 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
       vofs[db] = vr * D + 8 * ((4 * db + x) ^ fv) + 4 * (jl & 1);
   }
 
-  f32x16 acc[D / 32];
-  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[NB][D / 32];
+  float m_run[NB], l_run[NB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[nb][db] = f32x16{};
+  }
 
   const float c2 = p.scale_log2;
 
   const int n_full = min(max(n_past / kKeyTile - pt0, 0), npt);
   auto compute = [&](int t, const uint16_t* cK, const uint16_t* cV) {
-    // S^T = K Q^T for 64 keys x 32 queries
-    f32x16 S[2];
-    S[0] = f32x16{};
-    S[1] = f32x16{};
+    // S^T = K Q^T for 64 keys x (NB * 32) queries
+    f32x16 S[2][NB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) S[kb][nb] = f32x16{};
     // K fragments are read one d-step ahead of the products that use them
     auto kfrag = [&](int s, int kb) {
       return as_bf16x8(*reinterpret_cast<const u32x4*>(cK + kb * 32 * D + kofs[s % NKA] +
                                                        128 * (s / NKA)));
     };
+    // the product phase runs at raised wave priority: while this wave feeds the
+    // matrix cores, another resident wave's softmax work fills the gaps
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 ka0 = kfrag(0, 0), ka1 = kfrag(0, 1);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -258,20 +271,27 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         ka0 = kfrag(s + 1, 0);
         ka1 = kfrag(s + 1, 1);
       }
-      S[0] = mfma32(c0, qf[s], S[0]);
-      S[1] = mfma32(c1, qf[s], S[1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        S[0][nb] = mfma32(c0, qf[nb][s], S[0][nb]);
+        S[1][nb] = mfma32(c1, qf[nb][s], S[1][nb]);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
     const bool is_chunk = t >= npt;
     const int kbase = is_chunk ? (t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
     if (t >= n_full) {  // uniform: boundary and chunk tiles only
       // key kbase + 32 kb + acc_row(r, half) is masked when it reaches the limit;
       // the lane's offset is folded into one bound, the rest are immediates
-      const int lim = (is_chunk ? min(bcp, iq + 1) : n_past) - kbase - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const int lim = (is_chunk ? min(bcp, iq[nb] + 1) : n_past) - kbase - 4 * half;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) S[kb][r] = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) S[kb][nb][r] = -INFINITY;
+      }
     }
     // Lazy rescale: the reference maximum of a query only moves when a score
     // exceeds it by more than kSlack (base 2), so probabilities stay below
@@ -280,43 +300,47 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     // of a query (l and l ^ 32) take the same decision from the exchanged
     // maxima, so their halves of the key sum share one reference, and the
     // common case needs no exchange at all.
-    float mx = S[0][0];
+    bf16x8 P[NB][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = S[0][nb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    mx *= c2;
-    if (__any(mx > m_run + kSlack)) {
-      const float mq = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = mq > m_run + kSlack ? mq : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    // P^T operand: lane half h, 16-key group g16, slot e <-> key
-    // 16 g16 + 8 (e / 4) + 4 h + e % 4 (the accumulator row order of S^T)
-    bf16x8 P[4];
-    float ps = 0.f;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][nb][r]);
+      mx *= c2;
+      if (__any(mx > m_run[nb] + kSlack)) {
+        const float mq = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = mq > m_run[nb] + kSlack ? mq : m_run[nb];
+        const float alpha = m_run[nb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
 #pragma unroll
-    for (int g16 = 0; g16 < 4; ++g16) {
-      const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r0 + 2 * e], c2, -m_use));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r0 + 2 * e + 1], c2, -m_use));
-        ps += x0 + x1;
-        w[e] = pack_bf16x2(x0, x1);
+        for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
       }
-      P[g16] = as_bf16x8(w);
+      const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
+      // P^T operand: lane half h, 16-key group g16, slot e <-> key
+      // 16 g16 + 8 (e / 4) + 4 h + e % 4 (the accumulator row order of S^T)
+      float ps = 0.f;
+#pragma unroll
+      for (int g16 = 0; g16 < 4; ++g16) {
+        const int kb = g16 >> 1, r0 = 8 * (g16 & 1);
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e], c2, -m_use));
+          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][r0 + 2 * e + 1], c2, -m_use));
+          ps += x0 + x1;
+          w[e] = pack_bf16x2(x0, x1);
+        }
+        P[nb][g16] = as_bf16x8(w);
+      }
+      l_run[nb] += ps;
     }
-    l_run += ps;
     // O^T += V^T P^T, the key groups in order so that the products of the
     // first half can start while the second half's exponentials run; V^T
-    // operands come from transposed LDS reads, one product ahead
+    // operands come from transposed LDS reads, one product ahead, each used
+    // for the NB row blocks
     auto vfrag = [&](int n) {  // key group n / (D / 32), d block n % (D / 32)
       return lds_read_tr_pair(cV + vofs[n % (D / 32)] + (n / (D / 32)) * 16 * D, D);
     };
@@ -325,7 +349,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     for (int n = 0; n < D / 8; ++n) {
       const bf16x8 cur = va;
       if (n + 1 < D / 8) va = vfrag(n + 1);
-      acc[n % (D / 32)] = mfma32(cur, P[n / (D / 32)], acc[n % (D / 32)]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb][n % (D / 32)] = mfma32(cur, P[nb][n / (D / 32)], acc[nb][n % (D / 32)]);
     }
   };
 
@@ -353,14 +379,15 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   }
 
   // epilogue: lane (col, half) holds query col, d rows db*32 + 8*(r/4) + 4*half + r%4
-  {
-    const float lt = l_run + __shfl_xor(l_run, 32);
-    const int r = row0 + wave * 32 + col;
-    if (r >= M) return;
-    const int i = iq, g = r - (r / G) * G;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
+    const int r = row0 + (wave * NB + nb) * 32 + col;
+    if (r >= M) continue;
+    const int i = iq[nb], g = r - (r / G) * G;
     const size_t orow = (static_cast<size_t>(b) * p.nq + j * G + g) * bcp + i;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+    const float lse2 = lt > 0.f ? m_run[nb] + log2f(lt) : -INFINITY;
     if (p.n_split == 1) {
       uint16_t* op = p.out + orow * D;
 #pragma unroll
@@ -369,8 +396,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * half;
           uint2 w;
-          w.x = pack_bf16x2(acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv);
-          w.y = pack_bf16x2(acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv);
+          w.x = pack_bf16x2(acc[nb][db][4 * r4] * inv, acc[nb][db][4 * r4 + 1] * inv);
+          w.y = pack_bf16x2(acc[nb][db][4 * r4 + 2] * inv, acc[nb][db][4 * r4 + 3] * inv);
           *reinterpret_cast<uint2*>(op + d0) = w;
         }
       if (p.lse && half == 0) p.lse[orow] = lse2 * kLn2;
@@ -383,7 +410,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mag = fmaxf(mag, fabsf(acc[db][r]));
+        for (int rr = 0; rr < 16; ++rr) mag = fmaxf(mag, fabsf(acc[nb][db][rr]));
       mag = fmaxf(mag, __shfl_xor(mag, 32)) * inv;
       const float sc = mag > 0.f ? inv / mag : 0.f;
       uint32_t* op = p.part_o + (static_cast<size_t>(split) * rows_total + orow) * (D / 2);
@@ -393,8 +420,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * half;
           uint2 w;
-          w.x = pack_f16x2(acc[db][4 * r4] * sc, acc[db][4 * r4 + 1] * sc);
-          w.y = pack_f16x2(acc[db][4 * r4 + 2] * sc, acc[db][4 * r4 + 3] * sc);
+          w.x = pack_f16x2(acc[nb][db][4 * r4] * sc, acc[nb][db][4 * r4 + 1] * sc);
+          w.y = pack_f16x2(acc[nb][db][4 * r4 + 2] * sc, acc[nb][db][4 * r4 + 3] * sc);
           *reinterpret_cast<uint2*>(op + d0 / 2) = w;
         }
       if (half == 0) p.part_ls[static_cast<size_t>(split) * rows_total + orow] = float2{lse2, mag};
@@ -501,6 +528,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   if (lse) lse[orow] = m + logf(l);
 }
 
+// Row blocks per wave at d = 128.  One block and two waves per SIMD measured
+// faster than two blocks and one wave per SIMD (the accumulators of two
+// blocks overflow the architectural registers and shuttle through AGPRs).
+constexpr int kNB128 = 1;
+
 struct Plan {
   int waves, nb, rows, n_qtiles, n_split;
 };
@@ -510,14 +542,14 @@ Plan make_plan(int b, int nq, int nkv, int d, int bcp, int n_past_max) {
   const int G = nq / nkv;
   const int M = G * bcp;
   pl.waves = 4;
-  pl.nb = 1;
+  pl.nb = d == 128 ? kNB128 : 1;
   pl.rows = pl.waves * pl.nb * 32;
   pl.n_qtiles = (M + pl.rows - 1) / pl.rows;
   const int past_tiles = (n_past_max + kKeyTile - 1) / kKeyTile;
   const long long base = static_cast<long long>(pl.n_qtiles) * b * nkv;
   // key splits fill the resident slots (256 CUs x workgroups per CU) without
   // spilling into a second, mostly idle round; at least 4 key tiles per split
-  const long long slots = 256LL * (d == 256 ? 1 : 2);
+  const long long slots = 256LL * ((d == 256 || pl.nb == 2) ? 1 : 2);
   long long ns = slots / base;
   const long long max_split = past_tiles / 4 > 1 ? past_tiles / 4 : 1;
   if (ns > max_split) ns = max_split;
@@ -527,12 +559,12 @@ Plan make_plan(int b, int nq, int nkv, int d, int bcp, int n_past_max) {
   return pl;
 }
 
-template <int D, int WAVES, int OCC>
+template <int D, int NB, int WAVES, int OCC>
 hipError_t run_bf16(const AttnParams& p, int grid, hipStream_t st) {
   if (p.idx)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, OCC, true>), dim3(grid), dim3(64 * WAVES), 0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NB, WAVES, OCC, true>), dim3(grid), dim3(64 * WAVES), 0, st, p);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, OCC, false>), dim3(grid), dim3(64 * WAVES), 0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NB, WAVES, OCC, false>), dim3(grid), dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 
@@ -595,9 +627,9 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   }
   const int grid = pl.n_qtiles * c.b * c.nkv * pl.n_split;
   hipError_t e;
-  if (c.d == 128) e = run_bf16<128, 4, 2>(p, grid, st);
-  else if (c.d == 64) e = run_bf16<64, 4, 2>(p, grid, st);
-  else if (c.d == 256) e = run_bf16<256, 4, 1>(p, grid, st);
+  if (c.d == 128) e = run_bf16<128, kNB128, 4, kNB128 == 2 ? 1 : 2>(p, grid, st);
+  else if (c.d == 64) e = run_bf16<64, 1, 4, 2>(p, grid, st);
+  else if (c.d == 256) e = run_bf16<256, 1, 4, 1>(p, grid, st);
   else return hipErrorInvalidValue;
   if (e != hipSuccess || pl.n_split == 1) return e;
   const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4)), cblock(256);
