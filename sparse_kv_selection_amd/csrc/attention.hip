@@ -123,15 +123,20 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   const int n_past =
       __builtin_amdgcn_readfirstlane(min(p.sel_len ? p.sel_len[bj] : p.n_past, past_cap));
   const int past_tiles = (n_past + kKeyTile - 1) / kKeyTile;
-  // splits are balanced over this (b, KV head)'s own selection length
-  const int split_tiles = (past_tiles + p.n_split - 1) / p.n_split;
-  const int pt0 = split * split_tiles;
-  const int pt1 = min(pt0 + split_tiles, past_tiles);
-  const int npt = pt1 > pt0 ? pt1 - pt0 : 0;
   const int row0 = qtile * ROWS;
   const int i_max = (min(row0 + ROWS, M) - 1) / G;
-  const bool last = split == p.n_split - 1;
-  const int nct = last ? i_max / kKeyTile + 1 : 0;
+  // The key range of this row tile is the selected past tiles followed by the
+  // chunk tiles its queries reach (causal); the splits divide that combined
+  // range evenly (sizes differ by at most one tile), so the chunk tiles do not
+  // pile onto one split.
+  const int chunk_tiles = i_max / kKeyTile + 1;
+  const int total_tiles = past_tiles + chunk_tiles;
+  const int g0 = static_cast<int>(static_cast<long long>(split) * total_tiles / p.n_split);
+  const int g1 = static_cast<int>(static_cast<long long>(split + 1) * total_tiles / p.n_split);
+  const int pt0 = g0;                                   // first past tile
+  const int npt = max(0, min(g1, past_tiles) - g0);     // past tiles of this split
+  const int c0 = max(g0, past_tiles) - past_tiles;      // first chunk tile
+  const int nct = max(0, g1 - max(g0, past_tiles));     // chunk tiles of this split
   const int n_tiles = npt + nct;
 
   const uint16_t* pk = p.pk + static_cast<size_t>(bj) * p.past_bj_rows * D;
@@ -159,19 +164,19 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   // valid row; they are masked to -inf, so their weight is exactly 0.  Index
   // entries are loaded one tile ahead of the data loads that use them.
   int krow[IPW];
-  auto rows_of = [&](int t) {
+  auto rows_of = [&](int t, int* rr) {
     if (t < npt) {  // uniform
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int kk = min((pt0 + t) * kKeyTile + trow[i], n_past - 1);
-        krow[i] = IDX ? idx[kk] : kk;
+        rr[i] = IDX ? idx[kk] : kk;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) krow[i] = min((t - npt) * kKeyTile + trow[i], bcp - 1);
+      for (int i = 0; i < IPW; ++i) rr[i] = min((c0 + t - npt) * kKeyTile + trow[i], bcp - 1);
     }
   };
-  auto issue = [&](int t, uint16_t* dK, uint16_t* dV) {
+  auto issue = [&](int t, uint16_t* dK, uint16_t* dV, const int* rr) {
     const bool past = t < npt;
     const uint16_t* kbase = past ? pk : ck;
     const uint16_t* vbase = past ? pv : cv;
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       // one 32-bit byte offset from a wave-uniform base (scalar-base loads)
-      const uint32_t ro = static_cast<uint32_t>(min(max(krow[i], 0), hi)) * (2 * D);
+      const uint32_t ro = static_cast<uint32_t>(min(max(rr[i], 0), hi)) * (2 * D);
       uint16_t* lk = dK + (wave * IPW + i) * 512;
       uint16_t* lv = dV + (wave * IPW + i) * 512;
       lds_load16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kbase) +
@@ -190,6 +195,15 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
                  lv);
     }
   };
+
+  // The index entries of the first two tiles go out before the query loads:
+  // loads retire in order, so the first tile's copy then waits for its own
+  // indices only, while the query fragments are still in flight.
+  int krow0[IPW];
+  if (n_tiles > 0) {
+    rows_of(0, krow0);
+    if (n_tiles > 1) rows_of(1, krow);
+  }
 
   // query fragments: lane (col, half) holds row col of block nb, d slots
   // 16s + 8half + [0,8); a wave owns NB independent blocks of 32 rows, whose
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     }
     __builtin_amdgcn_s_setprio(0);
     const bool is_chunk = t >= npt;
-    const int kbase = is_chunk ? (t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
+    const int kbase = is_chunk ? (c0 + t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
     if (t >= n_full) {  // uniform: boundary and chunk tiles only
       // key kbase + 32 kb + acc_row(r, half) is masked when it reaches the limit;
       // the lane's offset is folded into one bound, the rest are immediates
@@ -359,17 +373,13 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   // everyone's via the barrier, which also retires all reads of tile t - 1),
   // start the loads of tile t + 1 into the other stage and the index loads of
   // tile t + 2, then compute tile t.
-  if (n_tiles > 0) {
-    rows_of(0);
-    issue(0, sK0, sV0);
-    if (n_tiles > 1) rows_of(1);
-  }
+  if (n_tiles > 0) issue(0, sK0, sV0, krow0);
   auto step = [&](int t, uint16_t* cK, uint16_t* cV, uint16_t* nK, uint16_t* nV) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's loads of tile t landed
     __syncthreads();
     if (t + 1 < n_tiles) {
-      issue(t + 1, nK, nV);
-      if (t + 2 < n_tiles) rows_of(t + 2);
+      issue(t + 1, nK, nV, krow);
+      if (t + 2 < n_tiles) rows_of(t + 2, krow);
     }
     if (wave_active) compute(t, cK, cV);
   };
