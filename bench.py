@@ -2,7 +2,7 @@
 the selected keys, on one MI355X.
 
 A step is the whole hot path over one chunk whose inputs are resident in HBM:
-    qk_qsel -> qk_kvscore -> qk_topk -> qk_sparse_attn_indexed
+    qk_qsel -> qk_kvscore_grouped -> qk_topk -> qk_sparse_attn_indexed
 (the gather of the selected rows is fused into the attention's loads).
 Steps rotate over several copies of the inputs (more bytes than the 256 MB
 Infinity Cache), so each step streams its K and V from HBM.
@@ -69,8 +69,10 @@ def algorithmic(spec, n_sel_per_bj):
     (sequence, KV head)."""
     esz = 2 if spec.dtype == "bf16" else 4
     bnkv = spec.b * spec.nkv
-    # scoring: every past key read once (d*esz) + one fp32 score written, plus the group queries
-    score_bytes = bnkv * spec.t_past * (spec.d * esz + 4) + bnkv * spec.nq_keep * spec.d * 4
+    # scoring: every past key read once (d*esz) + one fp32 score written, plus the kept
+    # query rows and their positions (the group queries are formed inside the pass)
+    score_bytes = (bnkv * spec.t_past * (spec.d * esz + 4)
+                   + spec.b * spec.nq * spec.nq_keep * (spec.d * esz + 4))
     score_flops = 2.0 * bnkv * spec.nq_keep * spec.d * spec.t_past
     # attention: 4*d flops per (query row, attended key); causal chunk counts its half
     rows = spec.b * spec.nq * spec.bcp
@@ -220,7 +222,7 @@ def main():
         ev[0].record()
         qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
         ev[1].record()
-        qk.qk_kvscore(shape, pipe.q_group, c["k"], pipe.s_agg)
+        qk.qk_kvscore_grouped(shape, c["q"], pipe.q_idx, c["k"], pipe.s_agg)
         ev[2].record()
         if rounds:
             qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"], spec.top_rounds,
@@ -240,7 +242,7 @@ def main():
     work = algorithmic(spec, n_sel)
     score_gbs = work["score_bytes"] / (stage_ms["kvscore"] * 1e-3) / 1e9
     attn_tflops = work["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
-    roof_score = {"kernel": "qk_kvscore (kvscore_bf16_kernel)", "bound": "hbm",
+    roof_score = {"kernel": "qk_kvscore_grouped (kvscore_bf16_kernel)", "bound": "hbm",
                   "achieved": round(score_gbs, 1),
                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                   "traffic": measured_traffic(spec.name, "kvscore"),

@@ -8,6 +8,8 @@
  *                   normalise and average over each GQA group
  *   qk_kvscore      cosine score of every past key against the group queries,
  *                   max over the kept queries
+ *   qk_kvscore_grouped  same, forming the group queries from the kept
+ *                   positions inside the scoring pass
  *   qk_topk         per-row top-k indices of fp32 scores (ascending order)
  *   qk_round_select round-granular variant: round score = max over the round,
  *                   keep the latest round plus the top rounds
@@ -124,7 +126,8 @@ size_t qk_workspace_bytes(const qk_shape* s, int32_t op);
  *                      lower position)
  *   q_group[b,j,n] = mean over g < G of q[b,jG+g,q_idx[b,jG+g,n]] / |.|
  * q: (b,nq,bcp,d) f32 or bf16.  q_idx: (b,nq,NQ) int32.  sq: (b,nq,bcp) f32 or
- * NULL.  q_group: (b,nkv,NQ,d) f32.  Arithmetic is fp32. */
+ * NULL.  q_group: (b,nkv,NQ,d) f32, or NULL to skip the group means (for
+ * qk_kvscore_grouped, which forms them itself).  Arithmetic is fp32. */
 qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq,
                   float* q_group, qk_stream_t stream);
 
@@ -135,6 +138,16 @@ qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq,
  * low part (about 2^-16 relative), fp32 accumulation.  f32: fp32 FMA. */
 qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k,
                      float* s_agg, qk_stream_t stream);
+
+/* Key scoring with the group queries formed inside the scoring pass (QUOKA
+ * write-up, section 2.3 listing: normalise the kept queries, average them over
+ * the GQA group, score every past key).  Equals qk_qsel's q_group followed by
+ * qk_kvscore, without the q_group round trip through memory and its launch.
+ * q: (b,nq,bcp,d), same dtype as k.  q_idx: (b,nq,NQ) int32 as written by
+ * qk_qsel; entries outside [0, bcp) are clamped into it.  Limits as qk_kvscore;
+ * f32 additionally needs NQ*(d+G)*4 <= 65536 bytes (else QK_ERR_UNSUPPORTED). */
+qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_idx,
+                             const void* k, float* s_agg, qk_stream_t stream);
 
 /* Per-row top-k of fp32 scores (QUOKA write-up, section 2.3: top-BSA keys per
  * KV head).  scores: (rows, n), row stride ld_scores >= n.  idx: (rows, k)

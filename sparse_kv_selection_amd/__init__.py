@@ -26,7 +26,8 @@ QK_F32, QK_BF16 = 0, 1
 OPS = {"qsel": 0, "kvscore": 1, "topk": 2, "round_select": 3, "gather": 4,
        "sparse_attn": 5, "dense_attn": 6}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
-            "qk_kvscore", "qk_topk", "qk_round_select", "qk_gather", "qk_sparse_attn",
+            "qk_kvscore", "qk_kvscore_grouped", "qk_topk", "qk_round_select", "qk_gather",
+            "qk_sparse_attn",
             "qk_sparse_attn_indexed", "qk_dense_attn"]
 
 
@@ -94,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_workspace_bytes": ([F, I], SZ),
         "qk_qsel": ([F, P, P, P, P, P], I),
         "qk_kvscore": ([F, P, P, P, P], I),
+        "qk_kvscore_grouped": ([F, P, P, P, P, P], I),
         "qk_topk": ([I, I, I, P, I, P, I, P, SZ, P], I),
         "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P], I),
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
@@ -160,6 +162,11 @@ def qk_kvscore(shape, q_group, k, s_agg, stream=None):
                                                     _ptr(s_agg), _stream(stream)))
 
 
+def qk_kvscore_grouped(shape, q, q_idx, k, s_agg, stream=None):
+    _check("qk_kvscore_grouped", load_library().qk_kvscore_grouped(
+        _sh(shape), _ptr(q), _ptr(q_idx), _ptr(k), _ptr(s_agg), _stream(stream)))
+
+
 def qk_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws=None, ws_bytes=0, stream=None):
     _check("qk_topk", load_library().qk_topk(rows, n, k, _ptr(scores), ld_scores, _ptr(idx),
                                               ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
@@ -216,19 +223,25 @@ class Pipeline:
     ``fused_gather``: attention reads the selected rows through the index list
     (qk_sparse_attn_indexed) instead of a qk_gather copy followed by
     qk_sparse_attn.
+
+    ``fused_group``: the scoring pass forms the group queries itself
+    (qk_kvscore_grouped); otherwise qk_qsel writes them to ``q_group`` and
+    qk_kvscore reads them.
     """
 
     def __init__(self, shape: Shape, device="cuda", n_rounds: int = 0, top_rounds: int = 0,
-                 keep_latest: bool = True, fused_gather: bool = True, with_lse: bool = True):
+                 keep_latest: bool = True, fused_gather: bool = True, with_lse: bool = True,
+                 fused_group: bool = True):
         s = self.shape = shape
         self.device = torch.device(device)
         self.n_rounds, self.top_rounds, self.keep_latest = n_rounds, top_rounds, keep_latest
-        self.fused_gather = fused_gather
+        self.fused_gather, self.fused_group = fused_gather, fused_group
         f32, i32 = torch.float32, torch.int32
         dev = self.device
         self.q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=i32, device=dev)
         self.sq = torch.empty((s.b, s.nq, s.bcp), dtype=f32, device=dev)
-        self.q_group = torch.empty((s.b, s.nkv, s.nq_keep, s.d), dtype=f32, device=dev)
+        self.q_group = (None if fused_group else
+                        torch.empty((s.b, s.nkv, s.nq_keep, s.d), dtype=f32, device=dev))
         self.s_agg = torch.empty((s.b, s.nkv, max(s.t_past, 1)), dtype=f32, device=dev)
         if n_rounds:
             self.ld_idx = max(s.t_past, 1)
@@ -246,10 +259,18 @@ class Pipeline:
         self.lse = torch.empty((s.b, s.nq, s.bcp), dtype=f32, device=dev) if with_lse else None
         self.ws, self.ws_bytes = _ws(s, "sparse_attn", dev)
 
-    def select(self, q, k, round_off=None):
+    def score(self, q, k):
+        """Query sub-selection and key scoring: q_idx, sq and s_agg."""
         s = self.shape
         qk_qsel(s, q, self.q_idx, self.sq, self.q_group)
-        qk_kvscore(s, self.q_group, k, self.s_agg)
+        if self.fused_group:
+            qk_kvscore_grouped(s, q, self.q_idx, k, self.s_agg)
+        else:
+            qk_kvscore(s, self.q_group, k, self.s_agg)
+
+    def select(self, q, k, round_off=None):
+        s = self.shape
+        self.score(q, k)
         if self.n_rounds:
             qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds,
                             self.keep_latest, self.idx, self.ld_idx, self.sel_len, self.s_round)

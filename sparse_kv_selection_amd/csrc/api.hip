@@ -57,6 +57,38 @@ qk_status check_ws(const qk_shape* s, int32_t op, const void* ws, size_t ws_byte
   return QK_OK;
 }
 
+qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
+                         const int32_t* q_idx, const void* k, float* s_agg, qk_stream_t stream) {
+  qk_status st = check_shape(s);
+  if (st != QK_OK) return st;
+  if (!k || !s_agg) return QK_ERR_NULL;
+  if (s->nq_keep < 1 || s->nq_keep > s->bcp) return QK_ERR_SHAPE;
+  if (is_bf16(s) ? (s->nq_keep > (s->d == 256 ? 32 : 64)) : (s->nq_keep * s->d > 16384))
+    return QK_ERR_UNSUPPORTED;
+  if (!is_bf16(s) && !q_group &&
+      qk::kvscore_f32_lds_bytes(s->d, s->nq_keep, s->nq / s->nkv) > 65536)
+    return QK_ERR_UNSUPPORTED;
+  if ((q_group && !aligned16(q_group)) || (q && !aligned16(q)) || (q_idx && !aligned4(q_idx)) ||
+      !aligned16(k) || !aligned4(s_agg))
+    return QK_ERR_ALIGN;
+  qk::ScoreCall c;
+  c.bf16 = is_bf16(s);
+  c.q_group = q_group;
+  c.q = q;
+  c.q_idx = q_idx;
+  c.k = k;
+  c.s_agg = s_agg;
+  c.b = s->b;
+  c.nq = s->nq;
+  c.nkv = s->nkv;
+  c.d = s->d;
+  c.bcp = s->bcp;
+  c.t_past = s->t_past;
+  c.kv_cap = s->kv_cap;
+  c.nq_keep = s->nq_keep;
+  return hip_status(qk::launch_kvscore(c, hs(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,9 +124,9 @@ qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq, f
                   qk_stream_t stream) {
   qk_status st = check_shape(s);
   if (st != QK_OK) return st;
-  if (!q || !q_idx || !q_group) return QK_ERR_NULL;
+  if (!q || !q_idx) return QK_ERR_NULL;
   if (s->nq_keep < 1 || s->nq_keep > s->bcp || s->nq_keep > 256) return QK_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(q_group) || !aligned4(q_idx) || (sq && !aligned4(sq)))
+  if (!aligned16(q) || (q_group && !aligned16(q_group)) || !aligned4(q_idx) || (sq && !aligned4(sq)))
     return QK_ERR_ALIGN;
   return hip_status(qk::launch_qsel(is_bf16(s), q, q_idx, sq, q_group, s->b, s->nq, s->nkv, s->d,
                                     s->bcp, s->nq_keep, hs(stream)));
@@ -102,15 +134,14 @@ qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq, f
 
 qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k, float* s_agg,
                      qk_stream_t stream) {
-  qk_status st = check_shape(s);
-  if (st != QK_OK) return st;
-  if (!q_group || !k || !s_agg) return QK_ERR_NULL;
-  if (s->nq_keep < 1 || s->nq_keep > s->bcp) return QK_ERR_SHAPE;
-  if (is_bf16(s) ? (s->nq_keep > (s->d == 256 ? 32 : 64)) : (s->nq_keep * s->d > 16384))
-    return QK_ERR_UNSUPPORTED;
-  if (!aligned16(q_group) || !aligned16(k) || !aligned4(s_agg)) return QK_ERR_ALIGN;
-  return hip_status(qk::launch_kvscore(is_bf16(s), q_group, k, s_agg, s->b, s->nkv, s->d,
-                                       s->t_past, s->kv_cap, s->nq_keep, hs(stream)));
+  if (!q_group) return QK_ERR_NULL;
+  return kvscore_common(s, q_group, nullptr, nullptr, k, s_agg, stream);
+}
+
+qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_idx,
+                             const void* k, float* s_agg, qk_stream_t stream) {
+  if (!q || !q_idx) return QK_ERR_NULL;
+  return kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream);
 }
 
 qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32_t ld_scores,

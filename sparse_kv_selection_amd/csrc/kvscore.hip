@@ -35,31 +35,130 @@ namespace {
 constexpr int kScoreWaves = 4;     // independent waves per workgroup
 constexpr int kBlock = 32;         // keys per block (one tile column set)
 
-template <int D, int NQB, int STAGES>
-__global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
-    const float* __restrict__ q_group, const uint16_t* __restrict__ k, float* __restrict__ s_agg,
-    int bnkv, int t_past, int kv_cap, int nq_keep, int blocks_per_bj, int blocks_per_wave) {
+struct ScoreArgs {
+  const float* q_group;    // (b, nkv, nq_keep, d) fp32, or nullptr: formed from q / q_idx
+  const uint16_t* q;       // (b, nq, bcp, d) the chunk's queries
+  const int32_t* q_idx;    // (b, nq, nq_keep) kept positions
+  const uint16_t* k;
+  float* s_agg;
+  int nkv, group, bcp, t_past, kv_cap, nq_keep;
+  int blocks_per_bj, wgs_per_bj;
+};
+
+// Group queries of one (b, KV head) formed by the whole workgroup (section 2.3
+// listing: the kept queries are L2-normalised, then averaged over the G heads
+// of the group), split into bf16 high and low parts in LDS.  Thread pair p =
+// (row n, 8-element chunk c); the CH threads of a row are adjacent lanes of
+// one wave, so a row norm is a shuffle sum.  The kept positions of the first
+// GB heads are loaded by load_pos before the caller issues its key loads.
+template <int D, int NQB>
+struct GroupBuild {
+  static constexpr int CH = D / 8;
+  static constexpr int ROWS = NQB * 32;
+  static constexpr int U = ROWS * CH / (64 * kScoreWaves);  // pairs per thread
+  static constexpr int GB = 4;                               // heads per batch
+  static constexpr int LD = D + 8;                           // padded LDS row (bf16)
+  static_assert(U >= 1 && (64 * kScoreWaves) % CH == 0, "pair layout");
+
+  int pos[U][GB];
+
+  __device__ __forceinline__ void load_pos(const ScoreArgs& a, int bj, int g0) {
+    const int b = bj / a.nkv, j = bj - b * a.nkv;
+    const int32_t* qi = a.q_idx + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.nq_keep;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = min((static_cast<int>(threadIdx.x) + 64 * kScoreWaves * u) / CH, a.nq_keep - 1);
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg) {
+        const int g = min(g0 + gg, a.group - 1);
+        pos[u][gg] = min(max(qi[g * a.nq_keep + n], 0), a.bcp - 1);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void build(const ScoreArgs& a, int bj, uint16_t* s_hi,
+                                        uint16_t* s_lo) {
+    const int b = bj / a.nkv, j = bj - b * a.nkv;
+    const uint16_t* qb = a.q + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.bcp * D;
+    const int c = threadIdx.x % CH;
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+    for (int g0 = 0; g0 < a.group; g0 += GB) {
+      if (g0 > 0) load_pos(a, bj, g0);
+      u32x4 x[U][GB];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+          const int g = min(g0 + gg, a.group - 1);
+          x[u][gg] = ld16(qb + (static_cast<size_t>(g) * a.bcp + pos[u][gg]) * D + 8 * c);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[2 * e] = bf16lo(x[u][gg][e]); v[2 * e + 1] = bf16hi(x[u][gg][e]); }
+          float n2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) n2 += v[e] * v[e];
+#pragma unroll
+          for (int o = CH / 2; o > 0; o >>= 1) n2 += __shfl_xor(n2, o);
+          const float inv = g0 + gg < a.group ? 1.0f / fmaxf(sqrtf(n2), kEps) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[u][e] += v[e] * inv;
+        }
+    }
+    const float inv_g = 1.0f / static_cast<float>(a.group);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = (static_cast<int>(threadIdx.x) + 64 * kScoreWaves * u) / CH;
+      u32x4 hi, lo;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = acc[u][2 * p] * inv_g, x1 = acc[u][2 * p + 1] * inv_g;
+        const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+        hi[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo[p] = pack_bf16x2(x0 - bf16_to_f32(h0), x1 - bf16_to_f32(h1));
+      }
+      if (n < a.nq_keep) {
+        *reinterpret_cast<u32x4*>(s_hi + n * LD + 8 * c) = hi;
+        *reinterpret_cast<u32x4*>(s_lo + n * LD + 8 * c) = lo;
+      }
+    }
+  }
+};
+
+template <int D, int NQB, int STAGES, bool GROUPED>
+__global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(ScoreArgs a) {
   constexpr int NS = D / 16;  // k-steps per key
+  using GBuild = GroupBuild<D, NQB>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int waves_per_bj = (blocks_per_bj + blocks_per_wave - 1) / blocks_per_wave;
-  const int gw = blockIdx.x * kScoreWaves + wave;
-  const int bj = gw / waves_per_bj;
+  // a workgroup's waves all score one (b, KV head)
+  const int bj = blockIdx.x / a.wgs_per_bj;
+  const int waves_per_bj = a.wgs_per_bj * kScoreWaves;
   // Wave wi of this (b, KV head) takes blocks wi, wi + W, wi + 2W, ... (W the
   // waves per head): at any moment the head's waves read neighbouring blocks,
   // so the concurrent streams spread over the HBM channels instead of every
   // wave sitting at the same offset of an equally aligned private run.
-  const int wi = gw % waves_per_bj;
-  const int nblk = wi < blocks_per_bj ? (blocks_per_bj - wi + waves_per_bj - 1) / waves_per_bj : 0;
-  if (bj >= bnkv || nblk == 0) return;
+  const int wi = (blockIdx.x - bj * a.wgs_per_bj) * kScoreWaves + wave;
+  const int nblk = wi < a.blocks_per_bj ? (a.blocks_per_bj - wi + waves_per_bj - 1) / waves_per_bj : 0;
   auto block_of = [&](int m) { return wi + m * waves_per_bj; };
 
-  const uint16_t* kb = k + static_cast<size_t>(bj) * kv_cap * D + 8 * half;
-  float* out = s_agg + static_cast<size_t>(bj) * t_past;
+  const uint16_t* kb = a.k + static_cast<size_t>(bj) * a.kv_cap * D + 8 * half;
+  float* out = a.s_agg + static_cast<size_t>(bj) * a.t_past;
+
+  GBuild gb;
+  if constexpr (GROUPED) gb.load_pos(a, bj, 0);  // kept positions first: a dependent trip
 
   u32x4 buf[STAGES][NS];
   auto load_block = [&](int blk, u32x4* dst) {
-    const int row = min(blk * kBlock + col, kv_cap - 1);
+    const int row = min(blk * kBlock + col, a.kv_cap - 1);
     const uint16_t* src = kb + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) dst[s] = ld16(src + 16 * s);
@@ -70,12 +169,30 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
     if (i < nblk) load_block(block_of(i), buf[i]);
 
   bf16x8 qhi[NQB][NS], qlo[NQB][NS];
-  {
-    const float* qg = q_group + static_cast<size_t>(bj) * nq_keep * D;
+  if constexpr (GROUPED) {
+    __shared__ __align__(16) uint16_t s_hi[GBuild::ROWS * GBuild::LD];
+    __shared__ __align__(16) uint16_t s_lo[GBuild::ROWS * GBuild::LD];
+    gb.build(a, bj, s_hi, s_lo);
+    __syncthreads();
+    if (nblk == 0) return;
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
       int row = mb * 32 + col;
-      if (row >= nq_keep) row = 0;
+      if (row >= a.nq_keep) row = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = row * GBuild::LD + 16 * s + 8 * half;
+        qhi[mb][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_hi + off));
+        qlo[mb][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_lo + off));
+      }
+    }
+  } else {
+    if (nblk == 0) return;
+    const float* qg = a.q_group + static_cast<size_t>(bj) * a.nq_keep * D;
+#pragma unroll
+    for (int mb = 0; mb < NQB; ++mb) {
+      int row = mb * 32 + col;
+      if (row >= a.nq_keep) row = 0;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float* src = qg + static_cast<size_t>(row) * D + 16 * s + 8 * half;
@@ -130,7 +247,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
     n2 += __shfl_xor(n2, 32);
     const int key = blk * kBlock + col;
     // m / max(|k|, eps) as m * rsqrt(max(|k|^2, eps^2))
-    if (half == 0 && key < t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+    if (half == 0 && key < a.t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
   };
 
   // unrolled ring: this wave's m-th block lives in buf[m % STAGES]
@@ -146,19 +263,43 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(
   }
 }
 
-// fp32 path: one thread per key, group queries staged in LDS.
-__global__ __launch_bounds__(256) void kvscore_f32_kernel(const float* __restrict__ q_group,
-                                                          const float* __restrict__ k,
-                                                          float* __restrict__ s_agg, int d,
-                                                          int t_past, int kv_cap, int nq_keep) {
-  extern __shared__ float sq[];  // [nq_keep * d]
-  const int bj = blockIdx.y;
-  const float* qg = q_group + static_cast<size_t>(bj) * nq_keep * d;
-  for (int e = threadIdx.x; e < nq_keep * d; e += blockDim.x) sq[e] = qg[e];
+// fp32 path: one thread per key, group queries staged in LDS (copied, or
+// formed from the kept queries as in the bf16 path: per (n, g) the inverse norm
+// of the kept row, then the mean of the normalised rows).
+__global__ __launch_bounds__(256) void kvscore_f32_kernel(ScoreCall c) {
+  extern __shared__ float sq[];  // [nq_keep * d] group queries, then [nq_keep * G] inverse norms
+  const int bj = blockIdx.y, d = c.d, nq_keep = c.nq_keep;
+  if (c.q_group) {
+    const float* qg = c.q_group + static_cast<size_t>(bj) * nq_keep * d;
+    for (int e = threadIdx.x; e < nq_keep * d; e += blockDim.x) sq[e] = qg[e];
+  } else {
+    const int G = c.nq / c.nkv, b = bj / c.nkv, j = bj - b * c.nkv;
+    const float* qb = static_cast<const float*>(c.q) + (static_cast<size_t>(b) * c.nq + j * G) * c.bcp * d;
+    const int32_t* qi = c.q_idx + (static_cast<size_t>(b) * c.nq + j * G) * nq_keep;
+    float* inv = sq + nq_keep * d;
+    auto row = [&](int n, int g) {
+      const int pos = min(max(qi[g * nq_keep + n], 0), c.bcp - 1);
+      return qb + (static_cast<size_t>(g) * c.bcp + pos) * d;
+    };
+    for (int e = threadIdx.x; e < nq_keep * G; e += blockDim.x) {
+      const float* r = row(e / G, e % G);
+      float n2 = 0.f;
+      for (int x = 0; x < d; ++x) n2 += r[x] * r[x];
+      inv[e] = 1.0f / fmaxf(sqrtf(n2), kEps);
+    }
+    __syncthreads();
+    const float inv_g = 1.0f / static_cast<float>(G);
+    for (int e = threadIdx.x; e < nq_keep * d; e += blockDim.x) {
+      const int n = e / d, x = e - n * d;
+      float acc = 0.f;
+      for (int g = 0; g < G; ++g) acc += row(n, g)[x] * inv[n * G + g];
+      sq[e] = acc * inv_g;
+    }
+  }
   __syncthreads();
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= t_past) return;
-  const float* kr = k + (static_cast<size_t>(bj) * kv_cap + t) * d;
+  if (t >= c.t_past) return;
+  const float* kr = static_cast<const float*>(c.k) + (static_cast<size_t>(bj) * c.kv_cap + t) * d;
   float n2 = 0.f;
   for (int e = 0; e < d; ++e) n2 += kr[e] * kr[e];
   float m = -INFINITY;
@@ -167,46 +308,64 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(const float* __restric
     for (int e = 0; e < d; ++e) dot += sq[n * d + e] * kr[e];
     m = fmaxf(m, dot);
   }
-  s_agg[static_cast<size_t>(bj) * t_past + t] = m / fmaxf(sqrtf(n2), kEps);
+  c.s_agg[static_cast<size_t>(bj) * c.t_past + t] = m / fmaxf(sqrtf(n2), kEps);
 }
 
 template <int D, int NQB>
-void launch_bf16(const float* qg, const uint16_t* k, float* s, int bnkv, int t_past, int kv_cap,
-                 int nq_keep, hipStream_t st) {
+void launch_bf16(const ScoreCall& c, hipStream_t st) {
   constexpr int STAGES = 4;
-  const int blocks_per_bj = (t_past + kBlock - 1) / kBlock;
+  const int bnkv = c.b * c.nkv;
+  ScoreArgs a;
+  a.q_group = c.q_group;
+  a.q = static_cast<const uint16_t*>(c.q);
+  a.q_idx = c.q_idx;
+  a.k = static_cast<const uint16_t*>(c.k);
+  a.s_agg = c.s_agg;
+  a.nkv = c.nkv;
+  a.group = c.nq / c.nkv;
+  a.bcp = c.bcp;
+  a.t_past = c.t_past;
+  a.kv_cap = c.kv_cap;
+  a.nq_keep = c.nq_keep;
+  a.blocks_per_bj = (c.t_past + kBlock - 1) / kBlock;
   // about as many waves as are resident (two per SIMD where the registers
   // allow, else one), each streaming its share of blocks
   constexpr long long kResident = (D == 256 || NQB > 1) ? 1024 : 2048;
-  const long long total = static_cast<long long>(blocks_per_bj) * bnkv;
+  const long long total = static_cast<long long>(a.blocks_per_bj) * bnkv;
   long long bpw = (total + kResident - 1) / kResident;
   if (bpw < 2) bpw = 2;
-  if (bpw > blocks_per_bj) bpw = blocks_per_bj;
-  const long long waves = ((blocks_per_bj + bpw - 1) / bpw) * static_cast<long long>(bnkv);
-  const int wgs = static_cast<int>((waves + kScoreWaves - 1) / kScoreWaves);
-  hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES>), dim3(wgs), dim3(64 * kScoreWaves), 0,
-                     st, qg, k, s, bnkv, t_past, kv_cap, nq_keep, blocks_per_bj, static_cast<int>(bpw));
+  if (bpw > a.blocks_per_bj) bpw = a.blocks_per_bj;
+  const long long waves_per_bj = (a.blocks_per_bj + bpw - 1) / bpw;
+  a.wgs_per_bj = static_cast<int>((waves_per_bj + kScoreWaves - 1) / kScoreWaves);
+  const dim3 grid(a.wgs_per_bj * bnkv), block(64 * kScoreWaves);
+  if (c.q_group)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true>), grid, block, 0, st, a);
 }
 
 }  // namespace
 
-hipError_t launch_kvscore(bool bf16, const float* q_group, const void* k, float* s_agg, int b,
-                          int nkv, int d, int t_past, int kv_cap, int nq_keep, hipStream_t st) {
-  const int bnkv = b * nkv;
-  if (t_past == 0) return hipSuccess;
-  if (!bf16) {
-    dim3 grid((t_past + 255) / 256, bnkv);
-    hipLaunchKernelGGL(kvscore_f32_kernel, grid, dim3(256), sizeof(float) * nq_keep * d, st,
-                       q_group, static_cast<const float*>(k), s_agg, d, t_past, kv_cap, nq_keep);
+size_t kvscore_f32_lds_bytes(int d, int nq_keep, int group) {
+  return sizeof(float) * (static_cast<size_t>(nq_keep) * d + static_cast<size_t>(nq_keep) * group);
+}
+
+hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st) {
+  const int bnkv = c.b * c.nkv;
+  if (c.t_past == 0) return hipSuccess;
+  if (!c.bf16) {
+    dim3 grid((c.t_past + 255) / 256, bnkv);
+    const size_t lds = c.q_group ? sizeof(float) * c.nq_keep * c.d
+                                 : kvscore_f32_lds_bytes(c.d, c.nq_keep, c.nq / c.nkv);
+    hipLaunchKernelGGL(kvscore_f32_kernel, grid, dim3(256), lds, st, c);
     return hipGetLastError();
   }
-  const uint16_t* kk = static_cast<const uint16_t*>(k);
-  const int nqb = (nq_keep + 31) / 32;
-  if (d == 128 && nqb == 1) launch_bf16<128, 1>(q_group, kk, s_agg, bnkv, t_past, kv_cap, nq_keep, st);
-  else if (d == 128 && nqb == 2) launch_bf16<128, 2>(q_group, kk, s_agg, bnkv, t_past, kv_cap, nq_keep, st);
-  else if (d == 64 && nqb == 1) launch_bf16<64, 1>(q_group, kk, s_agg, bnkv, t_past, kv_cap, nq_keep, st);
-  else if (d == 64 && nqb == 2) launch_bf16<64, 2>(q_group, kk, s_agg, bnkv, t_past, kv_cap, nq_keep, st);
-  else if (d == 256 && nqb == 1) launch_bf16<256, 1>(q_group, kk, s_agg, bnkv, t_past, kv_cap, nq_keep, st);
+  const int nqb = (c.nq_keep + 31) / 32;
+  if (c.d == 128 && nqb == 1) launch_bf16<128, 1>(c, st);
+  else if (c.d == 128 && nqb == 2) launch_bf16<128, 2>(c, st);
+  else if (c.d == 64 && nqb == 1) launch_bf16<64, 1>(c, st);
+  else if (c.d == 64 && nqb == 2) launch_bf16<64, 2>(c, st);
+  else if (c.d == 256 && nqb == 1) launch_bf16<256, 1>(c, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -10,9 +10,20 @@ namespace qk {
 hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group,
                        int b, int nq, int nkv, int d, int bcp, int nq_keep, hipStream_t st);
 
-// Key scoring pass.
-hipError_t launch_kvscore(bool bf16, const float* q_group, const void* k, float* s_agg, int b,
-                          int nkv, int d, int t_past, int kv_cap, int nq_keep, hipStream_t st);
+// Key scoring pass.  q_group == nullptr: the group queries are formed from
+// (q, q_idx) inside the scoring kernel.
+struct ScoreCall {
+  bool bf16;
+  const float* q_group;
+  const void* q;
+  const int32_t* q_idx;
+  const void* k;
+  float* s_agg;
+  int b, nq, nkv, d, bcp, t_past, kv_cap, nq_keep;
+};
+hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
+// LDS bytes of the fp32 scoring kernel when it forms the group queries itself.
+size_t kvscore_f32_lds_bytes(int d, int nq_keep, int group);
 
 // Per-row top-k, ascending indices.
 hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,

@@ -12,9 +12,10 @@
 //      per-row dot products and norms are reduced across the lanes that share
 //      a row, and one wave sorts the (score, position) keys with a bitonic
 //      network -- exact, deterministic, ties to the lower position;
-//   2. one wave per (sequence, KV head, slot n): the n-th kept query of each of
-//      the G heads is normalised and the G unit vectors are averaged in a fixed
-//      order.
+//   2. (when the group queries are asked for) one wave per (sequence, KV
+//      head, slot n): the n-th kept query of each of the G heads is normalised
+//      and the G unit vectors are averaged in a fixed order.  The scoring pass
+//      can form the same means itself from the kept positions instead.
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -347,8 +348,9 @@ hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, 
     else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
     else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
   }
-  hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
-                     static_cast<const T*>(q), q_idx, q_group, nq, nkv, bcp, nq_keep);
+  if (q_group)
+    hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
+                       static_cast<const T*>(q), q_idx, q_group, nq, nkv, bcp, nq_keep);
   return hipGetLastError();
 }
 

@@ -86,6 +86,12 @@ def test_null_and_alignment():
     assert lib.qk_qsel(ctypes.byref(s), _p(FAKE + 8), _p(), None, _p(), None) == ALIGN
     assert lib.qk_kvscore(ctypes.byref(s), _p(), _p(FAKE + 2), _p(), None) == ALIGN
     assert lib.qk_kvscore(ctypes.byref(s), _p(), None, _p(), None) == NULL
+    assert lib.qk_kvscore(ctypes.byref(s), None, _p(), _p(), None) == NULL
+    assert lib.qk_kvscore_grouped(ctypes.byref(s), None, _p(), _p(), _p(), None) == NULL
+    assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(), None, _p(), _p(), None) == NULL
+    assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(), _p(), _p(), None, None) == NULL
+    assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(FAKE + 4), _p(), _p(), _p(), None) == ALIGN
+    assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(), _p(FAKE + 2), _p(), _p(), None) == ALIGN
 
 
 @nogpu
@@ -93,6 +99,12 @@ def test_kvscore_limits():
     lib = qk.load_library()
     assert lib.qk_kvscore(ctypes.byref(_shape(nq_keep=65, bcp=128, kv_cap=2000)), _p(), _p(), _p(), None) == UNSUP
     assert lib.qk_kvscore(ctypes.byref(_shape(nq_keep=33, d=256)), _p(), _p(), _p(), None) == UNSUP
+    grouped = lib.qk_kvscore_grouped
+    assert grouped(ctypes.byref(_shape(nq_keep=33, d=256)), _p(), _p(), _p(), _p(), None) == UNSUP
+    # f32: NQ * (d + G) * 4 bytes of LDS at most 64 KiB
+    f32 = dict(dtype=qk.QK_F32, d=256, bcp=128, kv_cap=2000)
+    assert grouped(ctypes.byref(_shape(nq_keep=64, nq=64, nkv=2, **f32)), _p(), _p(), _p(), _p(),
+                   None) == UNSUP
 
 
 @nogpu

@@ -136,6 +136,43 @@ def test_kvscore(gpu, name):
     assert err <= 5e-5, f"precision regression: {err}"   # bf16 hi/lo split: ~1e-6
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_kvscore_grouped(gpu, name):
+    """Scoring with the group queries formed inside the pass, fed the oracle's
+    kept positions: matches the oracle's scores of its own group queries."""
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    q_idx = torch.from_numpy(ref["qidx"].astype(np.int32)).to(_dev())
+    s_agg = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    qk.qk_kvscore_grouped(s, g["q"], q_idx, g["k"], s_agg)
+    torch.cuda.synchronize()
+    _, want = oracle.key_scores(ref["q_group"], np64(case["k"]), s.t_past)
+    err = max_abs(s_agg, want)
+    assert err <= SCORE_TOL, err
+    assert err <= 5e-5, f"precision regression: {err}"
+
+
+def test_kvscore_grouped_matches_split_path(gpu):
+    """The fused scoring pass and qk_qsel's group means followed by qk_kvscore
+    agree (same kept positions), on a case with G = 8 (two position batches)
+    and 64 kept queries (two query tiles)."""
+    qk = gpu
+    spec = W.spec("long_128k", t_past=5000, bcp=160, nq_keep=64, bsa=512)
+    case = W.make_case(spec, 21)
+    s = qk.shape_of(spec)
+    g = {n: case[n].to(_dev()) for n in ("q", "k")}
+    q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=torch.int32, device=_dev())
+    qg = torch.empty((s.b, s.nkv, s.nq_keep, s.d), dtype=torch.float32, device=_dev())
+    qk.qk_qsel(s, g["q"], q_idx, None, qg)
+    a = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    b = torch.empty_like(a)
+    qk.qk_kvscore(s, qg, g["k"], a)
+    qk.qk_kvscore_grouped(s, g["q"], q_idx, g["k"], b)
+    torch.cuda.synchronize()
+    assert (a - b).abs().max().item() <= 1e-5
+
+
 # --------------------------------------------------------------------------
 # stage 3: top-BSA on the oracle's scores (fp32) -- integer result, exact
 # --------------------------------------------------------------------------
@@ -405,8 +442,15 @@ def test_deterministic(gpu):
     a(g["q"], g["k"], g["v"])
     b(g["q"], g["k"], g["v"])
     torch.cuda.synchronize()
-    for n in ("q_idx", "q_group", "s_agg", "idx", "out", "lse"):
+    for n in ("q_idx", "s_agg", "idx", "out", "lse"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+    c = qk.Pipeline(s, device=_dev(), fused_group=False)
+    d = qk.Pipeline(s, device=_dev(), fused_group=False)
+    c(g["q"], g["k"], g["v"])
+    d(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    for n in ("q_idx", "q_group", "s_agg", "idx", "out", "lse"):
+        assert torch.equal(getattr(c, n), getattr(d, n)), n
 
 
 def test_workspace_reuse_across_calls(gpu):
