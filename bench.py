@@ -229,7 +229,7 @@ def main():
                                True, pipe.idx, pipe.ld_idx, pipe.sel_len, pipe.s_round)
         else:
             qk.qk_topk(shape.b * shape.nkv, shape.t_past, shape.bsa, pipe.s_agg, shape.t_past,
-                       pipe.idx, pipe.ld_idx)
+                       pipe.idx, pipe.ld_idx, pipe.topk_ws, pipe.topk_ws_bytes)
         ev[3].record()
         pipe.attend(c["q"], c["k"], c["v"])
         ev[4].record()

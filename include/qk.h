@@ -154,7 +154,10 @@ qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_
  * int32, row stride ld_idx >= k: the k positions with the largest score (ties:
  * lower position; -0.0 equals +0.0), in ascending position order.  k > n acts
  * as n; positions k..ld_idx of each row are left untouched.  Needs
- * qk_workspace_bytes(QK_OP_TOPK) of scratch (currently none). */
+ * qk_workspace_bytes(QK_OP_TOPK) bytes of scratch (ws, 16-byte aligned; NULL
+ * allowed when that is 0): non-zero for rows longer than 16384 scores, and for
+ * fewer than 128 rows longer than 4096, where one row is spread over several
+ * workgroups.  n <= 8388608 (else QK_ERR_UNSUPPORTED). */
 qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores,
                   int32_t ld_scores, int32_t* idx, int32_t ld_idx, void* ws,
                   size_t ws_bytes, qk_stream_t stream);

@@ -167,7 +167,16 @@ def qk_kvscore_grouped(shape, q, q_idx, k, s_agg, stream=None):
         _sh(shape), _ptr(q), _ptr(q_idx), _ptr(k), _ptr(s_agg), _stream(stream)))
 
 
+def topk_workspace_bytes(rows: int, n: int) -> int:
+    """qk_workspace_bytes(QK_OP_TOPK) for `rows` rows of `n` scores."""
+    return qk_workspace_bytes(Shape(rows, 1, 1, 64, 1, n, n + 1, 1, 1), "topk")
+
+
 def qk_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws=None, ws_bytes=0, stream=None):
+    """ws=None: a workspace of the required size is allocated for this call."""
+    if ws is None:
+        ws_bytes = topk_workspace_bytes(rows, n)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device) if ws_bytes else None
     _check("qk_topk", load_library().qk_topk(rows, n, k, _ptr(scores), ld_scores, _ptr(idx),
                                               ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
 
@@ -258,6 +267,9 @@ class Pipeline:
         self.out = torch.empty((s.b, s.nq, s.bcp, s.d), dtype=s.torch_dtype, device=dev)
         self.lse = torch.empty((s.b, s.nq, s.bcp), dtype=f32, device=dev) if with_lse else None
         self.ws, self.ws_bytes = _ws(s, "sparse_attn", dev)
+        self.topk_ws_bytes = 0 if n_rounds else topk_workspace_bytes(s.b * s.nkv, s.t_past)
+        self.topk_ws = (torch.empty(self.topk_ws_bytes, dtype=torch.uint8, device=dev)
+                        if self.topk_ws_bytes else None)
 
     def score(self, q, k):
         """Query sub-selection and key scoring: q_idx, sq and s_agg."""
@@ -276,7 +288,7 @@ class Pipeline:
                             self.keep_latest, self.idx, self.ld_idx, self.sel_len, self.s_round)
         else:
             qk_topk(s.b * s.nkv, s.t_past, s.bsa, self.s_agg, self.s_agg.shape[-1], self.idx,
-                    self.ld_idx)
+                    self.ld_idx, self.topk_ws, self.topk_ws_bytes)
 
     def attend(self, q, k, v):
         s = self.shape

@@ -110,8 +110,8 @@ const char* qk_status_string(qk_status s) {
 }
 
 size_t qk_workspace_bytes(const qk_shape* s, int32_t op) {
-  if (op == QK_OP_TOPK || op == QK_OP_QSEL || op == QK_OP_KVSCORE || op == QK_OP_ROUND_SELECT ||
-      op == QK_OP_GATHER)
+  if (op == QK_OP_TOPK) return s ? qk::topk_workspace_bytes(s->b, s->t_past) : 0;
+  if (op == QK_OP_QSEL || op == QK_OP_KVSCORE || op == QK_OP_ROUND_SELECT || op == QK_OP_GATHER)
     return 0;
   if (check_shape(s) != QK_OK) return 0;
   if (op == QK_OP_SPARSE_ATTN || op == QK_OP_DENSE_ATTN)
@@ -146,15 +146,20 @@ qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_
 
 qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32_t ld_scores,
                   int32_t* idx, int32_t ld_idx, void* ws, size_t ws_bytes, qk_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (rows < 0 || n < 0 || k < 1 || ld_scores < n) return QK_ERR_SHAPE;
   const int kk = k < n ? k : n;
   if (ld_idx < kk) return QK_ERR_SHAPE;
   if (rows == 0 || n == 0) return QK_OK;
+  if (n > qk::topk_max_row()) return QK_ERR_UNSUPPORTED;
   if (!scores || !idx) return QK_ERR_NULL;
   if (!aligned4(scores) || !aligned4(idx)) return QK_ERR_ALIGN;
-  return hip_status(qk::launch_topk(rows, n, k, scores, ld_scores, idx, ld_idx, hs(stream)));
+  const size_t need = qk::topk_workspace_bytes(rows, n);
+  if (need > 0) {
+    if (!ws) return QK_ERR_NULL;
+    if (!aligned16(ws)) return QK_ERR_ALIGN;
+    if (ws_bytes < need) return QK_ERR_WORKSPACE;
+  }
+  return hip_status(qk::launch_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws, hs(stream)));
 }
 
 qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,

@@ -55,6 +55,26 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP steps: shifts
+// by 1, 2, 4 and 8 lanes inside each 16-lane row, then the end of row 0 (and
+// of row 2) is added to row 1 (row 3), and the end of row 1 to rows 2 and 3.
+// Lanes whose source lies outside the row keep the 0 they start from.  Every
+// lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return static_cast<uint32_t>(v);
+}
+// Value of lane 63 (for an inclusive scan: the wave total), uniform.
+__device__ __forceinline__ uint32_t lane63(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

@@ -25,9 +25,11 @@ hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
 // LDS bytes of the fp32 scoring kernel when it forms the group queries itself.
 size_t kvscore_f32_lds_bytes(int d, int nq_keep, int group);
 
-// Per-row top-k, ascending indices.
+// Per-row top-k, ascending indices.  ws: topk_workspace_bytes of scratch.
+size_t topk_workspace_bytes(int rows, int n);
+int topk_max_row();  // longest row qk_topk supports
 hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
-                       int ld_idx, hipStream_t st);
+                       int ld_idx, void* ws, hipStream_t st);
 
 // Round scores, selection and ragged expansion.
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,

@@ -4,11 +4,13 @@
 // aggregated score per KV head.  Ties go to the lower position and -0.0
 // equals +0.0, so the selected set is unique.
 //
-// One workgroup of 1024 threads per row; thread t owns the contiguous run
-// [t * ITEMS, (t + 1) * ITEMS) so that the output, in index order, needs one
-// block prefix sum.  The row stays in registers and the per-element work is
-// kept to a few instructions per phase, because a single CU's vector issue
-// rate bounds this kernel:
+// One workgroup of 1024 threads per row.  Layout: wave w covers the span
+// [w * 64 * ITEMS, (w + 1) * 64 * ITEMS) of the row in groups of 256
+// elements; lane l holds elements 4l .. 4l + 3 of each group, so every load
+// instruction of a wave reads 1 KiB contiguous and every store of selected
+// positions lands in a narrow window.  The row stays in registers and the
+// per-element work is kept to a few instructions per phase, because a single
+// CU's issue rate bounds this kernel:
 //   1. min / max of the row;
 //   2. histogram over 2048 equal-width value bins between min and max (the
 //      bin index is monotone in the value, so every bin above the one holding
@@ -19,9 +21,10 @@
 //   4. the exact threshold among them: each candidate is ranked against the
 //      others (an 8-bit radix select takes over for very large bins);
 //   5. compaction in index order: every element above the threshold, plus the
-//      first `need` elements equal to it, from one block prefix sum of packed
-//      (greater, equal) counts.
-// Rows longer than 32K scores are streamed from L2 in runs of 16 per pass.
+//      first `need` elements equal to it.  Output offsets come from one wave
+//      prefix sum per group of four elements and one block sum over waves.
+// Rows longer than 16K scores, and rows longer than 4K when there are too few
+// to fill the chip, take the split path below instead.
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -32,7 +35,6 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 4096;  // boundary-bin candidates kept in LDS
-constexpr int kRun = 16;     // elements per thread per streamed run
 
 // Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -44,43 +46,22 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Histograms are stored with one padding word per 32 bins, so that the lanes
+// of the crossing search, each reading a run of consecutive bins, hit
+// different LDS banks.
+constexpr int kHistWords = kBins + kBins / 32;
+__device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
+
 struct TopkShared {
-  int hist[kBins];
+  int hist[kHistWords];
   uint32_t cand[kCand];
-  int wsum[kTopkWaves];
+  uint32_t wsum[kTopkWaves];
   float red_min[kTopkWaves], red_max[kTopkWaves];
   int bin, above, cnt, need;
   uint32_t tau;
 };
 
-// Block-wide exclusive prefix sum over 1024 threads; *total gets the sum.
-__device__ int block_excl_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    int w = lane < kTopkWaves ? wsum[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < kTopkWaves; o <<= 1) {
-      const int y = __shfl_up(w, o);
-      if (lane >= o) w += y;
-    }
-    if (lane < kTopkWaves) wsum[lane] = w;
-  }
-  __syncthreads();
-  const int off = wave > 0 ? wsum[wave - 1] : 0;
-  *total = wsum[kTopkWaves - 1];
-  __syncthreads();
-  return off + x - v;
-}
-
-// Wave 0 only: the bin b of counts h[0..64 * PER) with
+// Wave 0 only: the bin b of counts h[hpad(0 .. 64 * PER)) with
 // count(bins > b) < need <= count(bins >= b); writes (*bin, *above) from the
 // lane that holds it.  Each lane keeps its PER bins in registers, so the search
 // is one batch of LDS reads, one wave scan and a register walk.
@@ -92,15 +73,10 @@ __device__ void wave_crossing(const int* h, int need, int* bin, int* above) {
   int sum = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    c[q] = h[top - q];
+    c[q] = h[hpad(top - q)];
     sum += c[q];
   }
-  int incl = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(sum)));
   const int ex = incl - sum;
   if (ex < need && need <= incl) {
     int b = top, a = ex;
@@ -143,10 +119,10 @@ __device__ void exact_threshold(TopkShared& sh, int need, VisitBin visit_bin) {
   uint32_t prefix = 0, pmask = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0;
+    for (int i = tid; i < hpad(256); i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
     auto count = [&](uint32_t kx) {
-      if ((kx & pmask) == prefix) atomicAdd(&sh.hist[(kx >> shift) & 255u], 1);
+      if ((kx & pmask) == prefix) atomicAdd(&sh.hist[hpad((kx >> shift) & 255u)], 1);
     };
     if (in_lds) {
       for (int c = tid; c < ncand; c += kTopkThreads) count(sh.cand[c]);
@@ -168,13 +144,109 @@ __device__ void exact_threshold(TopkShared& sh, int need, VisitBin visit_bin) {
   __syncthreads();
 }
 
-// Rows of n <= 1024 * ITEMS held in registers.
+// Position of element e (0 <= e < ITEMS) of this thread in a tile of
+// 1024 * ITEMS elements starting at `base`.
 template <int ITEMS>
+__device__ __forceinline__ int tile_pos(int base, int e) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return base + wave * 64 * ITEMS + (e >> 2) * 256 + 4 * lane + (e & 3);
+}
+
+// Loads this thread's elements of the tile at `base` (-inf beyond n); the
+// returned mask has bit e set for real elements.  Branch-free, so that all
+// loads are in flight together: addresses past the row are clamped into it.
+// VEC (rows 16-byte aligned, n a multiple of 4): one 16-byte load per group.
+template <int ITEMS, bool VEC>
+__device__ __forceinline__ uint32_t load_tile(const float* s, int base, int n, float* x) {
+  uint32_t valid = 0;
+#pragma unroll
+  for (int m = 0; m < ITEMS / 4; ++m) {
+    const int p = tile_pos<ITEMS>(base, 4 * m);
+    if constexpr (VEC) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(s + min(p, n - 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * m + j] = p < n ? v[j] : -INFINITY;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = s[min(p + j, n - 1)];
+        x[4 * m + j] = p + j < n ? v : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) valid |= static_cast<uint32_t>(p + j < n) << (4 * m + j);
+  }
+  return valid;
+}
+
+// Writes, in ascending position order, the positions of the tile's elements
+// in gmask (above the threshold) and the first elements of emask (equal to
+// it) while fewer than `need` equal elements have been taken in the whole row.
+// (base_gt, base_eq) count the elements of earlier tiles and are advanced by
+// this tile's totals.  Every thread of the block calls this.
+template <int ITEMS>
+__device__ void write_picks(uint32_t gmask, uint32_t emask, int base, int need, int k,
+                            int32_t* out, uint32_t* wsum, int& base_gt, int& base_eq) {
+  constexpr int M = ITEMS / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // packed (greater | equal << 16) counts; a tile holds at most 32768 elements
+  uint32_t pre[M];
+  uint32_t run = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t c = static_cast<uint32_t>(__popc((gmask >> (4 * m)) & 15u)) |
+                       (static_cast<uint32_t>(__popc((emask >> (4 * m)) & 15u)) << 16);
+    const uint32_t incl = wave_incl_scan(c);
+    pre[m] = run + incl - c;
+    run += lane63(incl);
+  }
+  if (lane == 0) wsum[wave] = run;
+  __syncthreads();
+  uint32_t woff = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t v = wsum[w];
+    woff += w < wave ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();  // wsum is reused by the next call
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t ex = woff + pre[m];
+    const int eq_before = base_eq + static_cast<int>(ex >> 16);
+    const int gt_before = base_gt + static_cast<int>(ex & 0xffffu);
+    const uint32_t g4 = (gmask >> (4 * m)) & 15u, e4 = (emask >> (4 * m)) & 15u;
+    int take = need - eq_before;
+    take = take < 0 ? 0 : min(take, __popc(e4));
+    uint32_t keep = 0, rest = e4;
+    for (int t = 0; t < take; ++t) {  // the lowest `take` equal elements
+      keep |= rest & (0u - rest);
+      rest &= rest - 1u;
+    }
+    const uint32_t pick = g4 | keep;
+    if (pick) {
+      int pos = gt_before + min(need, eq_before);
+      const int p0 = tile_pos<ITEMS>(base, 4 * m);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((pick >> j) & 1u) {
+          if (pos < k) out[pos] = p0 + j;
+          ++pos;
+        }
+      }
+    }
+  }
+  base_gt += static_cast<int>(tot & 0xffffu);
+  base_eq += static_cast<int>(tot >> 16);
+}
+
+// Rows of n <= 1024 * ITEMS held in registers.
+template <int ITEMS, bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __restrict__ scores,
                                                                 int n, int k, int ld_scores,
                                                                 int32_t* __restrict__ idx,
                                                                 int ld_idx) {
-  static_assert(ITEMS % 4 == 0 && ITEMS <= 32, "items per thread");
+  static_assert(ITEMS % 4 == 0 && ITEMS <= 16, "items per thread");
   __shared__ TopkShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* s = scores + static_cast<size_t>(blockIdx.x) * ld_scores;
@@ -185,29 +257,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
     for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
     return;
   }
-  const int i0 = tid * ITEMS;
-  const int nv = max(0, min(ITEMS, n - i0));  // real elements of this thread
-  const bool vec = ((ld_scores & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
 
   float x[ITEMS];
-  if (vec && nv == ITEMS) {
-#pragma unroll
-    for (int m = 0; m < ITEMS / 4; ++m) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(s + i0 + 4 * m);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * m + e] = v[e];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < ITEMS; ++e) x[e] = e < nv ? s[i0 + e] : -INFINITY;
-  }
+  const uint32_t valid = load_tile<ITEMS, VEC>(s, 0, n, x);
 
   // 1. min / max (padding is -inf: it never lowers the max; the min skips it)
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
     mx = fmaxf(mx, x[e]);
-    mn = fminf(mn, e < nv ? x[e] : INFINITY);
+    mn = fminf(mn, ((valid >> e) & 1u) ? x[e] : INFINITY);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -215,7 +274,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
     mx = fmaxf(mx, __shfl_xor(mx, o));
   }
   if (lane == 0) { sh.red_min[wave] = mn; sh.red_max[wave] = mx; }
-  for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+  for (int i = tid; i < kHistWords; i += kTopkThreads) sh.hist[i] = 0;
   if (tid == 0) { sh.cnt = 0; sh.bin = 0; sh.above = 0; sh.need = 1; sh.tau = 0u; }
   __syncthreads();
   mn = sh.red_min[0];
@@ -227,13 +286,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
   const float boff = -mn * bscale;
 
   // 2. histogram; bins kept packed two per register (padding lands in bin 0
-  //    and is counted there, harmlessly: k <= n)
+  //    and is counted there, harmlessly: k < n)
   uint32_t bins[ITEMS / 2];
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
     int b = static_cast<int>(__builtin_fmaf(x[e], bscale, boff));
     b = max(0, min(b, kBins - 1));
-    atomicAdd(&sh.hist[b], 1);
+    atomicAdd(&sh.hist[hpad(b)], 1);
     if (e & 1) bins[e >> 1] |= static_cast<uint32_t>(b) << 16;
     else bins[e >> 1] = static_cast<uint32_t>(b);
   }
@@ -248,19 +307,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
     const uint32_t b = (bins[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-    cmask |= static_cast<uint32_t>((b == B) & (e < nv)) << e;
+    cmask |= static_cast<uint32_t>(b == B) << e;
   }
+  cmask &= valid;
   {
     const int cnt = __popc(cmask);
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(cnt)));
     int base = 0;
     if (lane == 63 && incl > 0) base = atomicAdd(&sh.cnt, incl);
-    base = __shfl(base, 63) + incl - cnt;
+    base = static_cast<int>(lane63(static_cast<uint32_t>(base))) + incl - cnt;
     if (cmask) {
 #pragma unroll
       for (int e = 0; e < ITEMS; ++e) {
@@ -287,192 +342,327 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
     gmask |= static_cast<uint32_t>(x[e] > tau) << e;
-    emask |= static_cast<uint32_t>((x[e] == tau) & (e < nv)) << e;
+    emask |= static_cast<uint32_t>(x[e] == tau) << e;
   }
-  const int gt = __popc(gmask), eq = __popc(emask);
-  int tot;
-  const int ex = block_excl_scan(gt | (eq << 16), sh.wsum, &tot);
-  const int eq_before = ex >> 16;
-  int take = need - eq_before;
-  take = take < 0 ? 0 : (take > eq ? eq : take);
-  if (gt + take > 0) {
-    int pos = (ex & 0xffff) + min(need, eq_before);
-    // keep the first `take` equal elements of this thread
-    uint32_t keep = emask;
-    for (int drop = eq - take; drop > 0; --drop) keep &= ~(0x80000000u >> __clz(keep));
-    const uint32_t pick = gmask | keep;
+  int base_gt = 0, base_eq = 0;
+  write_picks<ITEMS>(gmask, emask & valid, 0, need, k, out, sh.wsum, base_gt, base_eq);
+}
+
+// k >= n: every position, in order.
+__global__ __launch_bounds__(256) void topk_all_kernel(int n, int32_t* __restrict__ idx, int ld_idx) {
+  int32_t* out = idx + static_cast<size_t>(blockIdx.y) * ld_idx;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) out[i] = i;
+}
+
+// ---------------------------------------------------------------------------
+// Split path for rows that are few or long: one row is spread over `slices`
+// workgroups of 1024 threads, each owning a tile of 1024 * IPT elements.
+//   pass 1 (topk_hist_kernel): each workgroup counting-sorts its tile by the
+//     top 11 bits of the order-preserving key: it writes the tile's histogram,
+//     its exclusive prefix, and the tile's (key, position) pairs grouped by
+//     bin (workspace; nothing needs initialising);
+//   pass 2 (topk_split_kernel): each workgroup sums the row's histograms and
+//     finds the boundary bin B, reads bin B's pairs from every tile's groups
+//     into LDS, fixes the remaining 21 key bits of the k-th largest key with
+//     two more radix levels over them, counts what earlier tiles contribute,
+//     and writes the positions picked in its own tile.
+// Workspace, for W = rows * slices workgroups: W histograms, W prefixes
+// (2048 ints each), then W tiles of (key, position) pairs.
+// ---------------------------------------------------------------------------
+constexpr int kL1Shift = 21;       // level-1 bin = key >> 21 (2048 bins)
+constexpr int kSplitCand = 6144;   // bin-B pairs kept in LDS
+constexpr int kCandPerThread = kSplitCand / kTopkThreads;
+
+template <int IPT, bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __restrict__ scores,
+                                                                 int n, int ld_scores, int slices,
+                                                                 int* __restrict__ part) {
+  __shared__ int h[kBins];
+  __shared__ int wtot[kTopkWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int w = blockIdx.x, nwg = gridDim.x;
+  const int row = w / slices, sl = w - row * slices;
+  const float* s = scores + static_cast<size_t>(row) * ld_scores;
+  constexpr int kTile = kTopkThreads * IPT;
+  for (int i = tid; i < kBins; i += kTopkThreads) h[i] = 0;
+  float x[IPT];
+  const uint32_t valid = load_tile<IPT, VEC>(s, sl * kTile, n, x);
+  uint32_t kx[IPT];
 #pragma unroll
-    for (int e = 0; e < ITEMS; ++e) {
-      if ((pick >> e) & 1u) {
-        if (pos < k) out[pos] = i0 + e;
-        ++pos;
-      }
+  for (int e = 0; e < IPT; ++e) kx[e] = fkey(x[e]);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    if ((valid >> e) & 1u) atomicAdd(&h[kx[e] >> kL1Shift], 1);
+  __syncthreads();
+  // exclusive prefix over the bins; thread t owns bins 2t and 2t + 1
+  const int c0 = h[2 * tid], c1 = h[2 * tid + 1];
+  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c0 + c1)));
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int v = 0; v < kTopkWaves; ++v) off += v < wave ? wtot[v] : 0;
+  const int ex = off + incl - c0 - c1;
+  *reinterpret_cast<int2*>(part + static_cast<size_t>(w) * kBins + 2 * tid) = int2{c0, c1};
+  *reinterpret_cast<int2*>(part + (static_cast<size_t>(nwg) + w) * kBins + 2 * tid) = int2{ex, ex + c0};
+  h[2 * tid] = ex;  // now the bins' write cursors (each thread rewrites only its own bins)
+  h[2 * tid + 1] = ex + c0;
+  __syncthreads();
+  uint2* pairs = reinterpret_cast<uint2*>(part + 2 * static_cast<size_t>(nwg) * kBins) +
+                 static_cast<size_t>(w) * kTile;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    if ((valid >> e) & 1u) {
+      const int slot = atomicAdd(&h[kx[e] >> kL1Shift], 1);
+      if (slot < kTile)  // always: the slots of a bin end where the next bin's begin
+        pairs[slot] = uint2{kx[e], static_cast<uint32_t>(tile_pos<IPT>(sl * kTile, e))};
     }
   }
 }
 
-// Longer rows: runs of kRun elements per thread, super-tile r covering
-// [r * 1024 * kRun, (r + 1) * 1024 * kRun), re-read (from L2) for each pass.
-__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(const float* __restrict__ scores,
-                                                                   int n, int k, int ld_scores,
-                                                                   int32_t* __restrict__ idx,
-                                                                   int ld_idx) {
-  __shared__ TopkShared sh;
+constexpr int kMaxSlices = 1024;
+
+struct SplitShared {
+  int hist[kHistWords];       // the row's level-1 histogram
+  int hist2[kHistWords];      // bits 20..10 of bin B's keys
+  int hist3[kHistWords / 2];  // bits 9..0
+  uint32_t ckey[kSplitCand];
+  int cpos[kSplitCand];
+  int seg_start[kMaxSlices + 1];  // bin B's pairs of tile t: [seg_start[t], seg_start[t + 1])
+  int seg_off[kMaxSlices];        // ... found at this offset in tile t's sorted pairs
+  uint32_t wsum[kTopkWaves];
+  int red[2][kTopkWaves];
+  int bin[3], above[3];
+};
+
+// Sum over the block of (a, b); every thread gets the totals.
+__device__ __forceinline__ void block_sum2(int& a, int& b, int (*red)[kTopkWaves]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = static_cast<int>(lane63(wave_incl_scan(static_cast<uint32_t>(a))));
+  b = static_cast<int>(lane63(wave_incl_scan(static_cast<uint32_t>(b))));
+  if (lane == 0) { red[0][wave] = a; red[1][wave] = b; }
+  __syncthreads();
+  a = 0;
+  b = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) { a += red[0][w]; b += red[1][w]; }
+  __syncthreads();
+}
+
+
+template <int IPT, bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* __restrict__ scores,
+                                                                  int n, int k, int ld_scores,
+                                                                  int slices,
+                                                                  const int* __restrict__ part,
+                                                                  int32_t* __restrict__ idx,
+                                                                  int ld_idx) {
+  __shared__ SplitShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* s = scores + static_cast<size_t>(blockIdx.x) * ld_scores;
-  int32_t* out = idx + static_cast<size_t>(blockIdx.x) * ld_idx;
-  if (k > n) k = n;
-  if (k <= 0) return;
-  if (k == n) {
-    for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
-    return;
-  }
-  const bool vec = ((ld_scores & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
-  constexpr int kSuper = kTopkThreads * kRun;
-  // calls g(x, i0, nv) for each run of this thread, in row order
-  auto runs = [&](auto g) {
-    for (int base = 0; base < n; base += kSuper) {
-      const int i0 = base + tid * kRun;
-      const int nv = max(0, min(kRun, n - i0));
-      float x[kRun];
-      if (vec && nv == kRun) {
+  const int row = blockIdx.x / slices, sl = blockIdx.x - row * slices;
+  const float* s = scores + static_cast<size_t>(row) * ld_scores;
+  int32_t* out = idx + static_cast<size_t>(row) * ld_idx;
+  const int p0 = sl * kTopkThreads * IPT;  // first position of this workgroup's tile
+  const int* prow = part + static_cast<size_t>(row) * slices * kBins;
+
+  // Its own tile and the row's tile histograms are requested together
+  // (batches of 8 tiles, addresses clamped so that a batch is branch-free).
+  float xo[IPT];
+  const uint32_t vo = load_tile<IPT, VEC>(s, p0, n, xo);
+  constexpr int U = kBins / kTopkThreads;
+  constexpr int kBatch = 8;
+  int total[U], before[U];
 #pragma unroll
-        for (int m = 0; m < kRun / 4; ++m) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(s + i0 + 4 * m);
+  for (int u = 0; u < U; ++u) { total[u] = 0; before[u] = 0; }
+  for (int s0 = 0; s0 < slices; s0 += kBatch) {
+    int v[kBatch][U];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * m + e] = v[e];
-        }
-      } else {
+    for (int i = 0; i < kBatch; ++i)
 #pragma unroll
-        for (int e = 0; e < kRun; ++e) x[e] = e < nv ? s[i0 + e] : -INFINITY;
+      for (int u = 0; u < U; ++u)
+        v[i][u] = prow[static_cast<size_t>(min(s0 + i, slices - 1)) * kBins + tid + kTopkThreads * u];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = s0 + i < slices ? v[i][u] : 0;
+        total[u] += c;
+        before[u] += s0 + i < sl ? c : 0;
       }
-      g(x, i0, nv);
+  }
+
+  // 1. boundary bin B of the row; bins above it in earlier tiles
+#pragma unroll
+  for (int u = 0; u < U; ++u) sh.hist[hpad(tid + kTopkThreads * u)] = total[u];
+  for (int i = tid; i < kHistWords; i += kTopkThreads) sh.hist2[i] = 0;
+  for (int i = tid; i < kHistWords / 2; i += kTopkThreads) sh.hist3[i] = 0;
+  __syncthreads();
+  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin[0], &sh.above[0]);
+  __syncthreads();
+  const uint32_t B = static_cast<uint32_t>(min(max(sh.bin[0], 0), kBins - 1));
+  int need = k - sh.above[0];
+  const int nb = sh.hist[hpad(B)];
+  int above_before = 0, unused = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    above_before += static_cast<uint32_t>(tid + kTopkThreads * u) > B ? before[u] : 0;
+
+  // 2. bin B's pairs of every tile -> LDS when they fit (else every visit
+  //    below reads them from the workspace)
+  if (tid < slices) {
+    const size_t t = static_cast<size_t>(row) * slices + tid;
+    sh.seg_start[tid + 1] = part[t * kBins + B];
+    sh.seg_off[tid] = part[(static_cast<size_t>(gridDim.x) + t) * kBins + B];
+  }
+  __syncthreads();
+  if (wave == 0) {  // inclusive scan of the tiles' counts
+    int carry = 0;
+    for (int t0 = 0; t0 < slices; t0 += 64) {
+      const int c = static_cast<int>(
+          wave_incl_scan(static_cast<uint32_t>(t0 + lane < slices ? sh.seg_start[t0 + lane + 1] : 0)));
+      if (t0 + lane < slices) sh.seg_start[t0 + lane + 1] = carry + c;
+      carry += static_cast<int>(lane63(static_cast<uint32_t>(c)));
+    }
+    if (lane == 0) sh.seg_start[0] = 0;
+  }
+  __syncthreads();
+  const uint2* pairs = reinterpret_cast<const uint2*>(part + 2 * static_cast<size_t>(gridDim.x) * kBins);
+  constexpr int kTile = kTopkThreads * IPT;
+  auto fetch = [&](int i) {  // the i-th pair of bin B, 0 <= i < nb
+    int lo = 0, hi = slices - 1;  // the tile t with seg_start[t] <= i < seg_start[t + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.seg_start[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int at = min(max(sh.seg_off[lo] + (i - sh.seg_start[lo]), 0), kTile - 1);
+    return pairs[(static_cast<size_t>(row) * slices + lo) * kTile + at];
+  };
+  const bool in_lds = nb <= kSplitCand;
+  if (in_lds) {
+    uint2 c[kCandPerThread];
+#pragma unroll
+    for (int r = 0; r < kCandPerThread; ++r) c[r] = fetch(min(tid + kTopkThreads * r, nb - 1));
+#pragma unroll
+    for (int r = 0; r < kCandPerThread; ++r) {
+      const int i = tid + kTopkThreads * r;
+      if (i < nb) {
+        sh.ckey[i] = c[r].x;
+        sh.cpos[i] = static_cast<int>(c[r].y);
+      }
+    }
+  }
+  block_sum2(above_before, unused, sh.red);  // also orders the LDS list before its reads
+  auto visit = [&](auto f) {  // f(key, position) for every element of bin B
+    if (in_lds) {
+      for (int i = tid; i < nb; i += kTopkThreads) f(sh.ckey[i], sh.cpos[i]);
+    } else {
+      for (int i = tid; i < nb; i += kTopkThreads) {
+        const uint2 c = fetch(i);
+        f(c.x, static_cast<int>(c.y));
+      }
     }
   };
 
-  float mn = INFINITY, mx = -INFINITY;
-  runs([&](const float* x, int, int nv) {
-#pragma unroll
-    for (int e = 0; e < kRun; ++e) {
-      mx = fmaxf(mx, x[e]);
-      mn = fminf(mn, e < nv ? x[e] : INFINITY);
+  // 3. the k-th largest key: bits 20..10, then bits 9..0, from histograms of bin B
+  visit([&](uint32_t kx, int) { atomicAdd(&sh.hist2[hpad((kx >> 10) & 2047u)], 1); });
+  __syncthreads();
+  if (wave == 0) wave_crossing<2048 / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
+  __syncthreads();
+  need -= sh.above[1];
+  const uint32_t prefix = (B << kL1Shift) | (static_cast<uint32_t>(min(max(sh.bin[1], 0), 2047)) << 10);
+  visit([&](uint32_t kx, int) {
+    if ((kx & 0xfffffc00u) == prefix) atomicAdd(&sh.hist3[hpad(kx & 1023u)], 1);
+  });
+  __syncthreads();
+  if (wave == 0) wave_crossing<1024 / 64>(sh.hist3, need, &sh.bin[2], &sh.above[2]);
+  __syncthreads();
+  need -= sh.above[2];
+  const uint32_t tau = prefix | static_cast<uint32_t>(min(max(sh.bin[2], 0), 1023));
+  // tau is the k-th largest key; `need` copies of it are taken (lowest positions first)
+
+  // 4. what earlier tiles contribute: greater keys and copies of tau
+  int gt_before = 0, eq_before = 0;
+  visit([&](uint32_t kx, int pos) {
+    if (pos < p0) {
+      gt_before += kx > tau;
+      eq_before += kx == tau;
     }
   });
+  block_sum2(gt_before, eq_before, sh.red);
+  gt_before += above_before;
+
+  // 5. this tile's picks, in position order
+  uint32_t gmask = 0, emask = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
+  for (int e = 0; e < IPT; ++e) {
+    const uint32_t kx = fkey(xo[e]);
+    gmask |= static_cast<uint32_t>(kx > tau) << e;
+    emask |= static_cast<uint32_t>(kx == tau) << e;
   }
-  if (lane == 0) { sh.red_min[wave] = mn; sh.red_max[wave] = mx; }
-  for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
-  if (tid == 0) { sh.cnt = 0; sh.bin = 0; sh.above = 0; sh.need = 1; sh.tau = 0u; }
-  __syncthreads();
-  mn = sh.red_min[0];
-  mx = sh.red_max[0];
-#pragma unroll
-  for (int w = 1; w < kTopkWaves; ++w) { mn = fminf(mn, sh.red_min[w]); mx = fmaxf(mx, sh.red_max[w]); }
-  float bscale = static_cast<float>(kBins) / (mx - mn);
-  if (!(bscale < INFINITY)) bscale = 0.f;
-  const float boff = -mn * bscale;
-  auto bin_of = [&](float v) {
-    const int b = static_cast<int>(__builtin_fmaf(v, bscale, boff));
-    return static_cast<uint32_t>(max(0, min(b, kBins - 1)));
-  };
+  write_picks<IPT>(gmask & vo, emask & vo, p0, need, k, out, sh.wsum, gt_before, eq_before);
+}
 
-  runs([&](const float* x, int, int) {
-#pragma unroll
-    for (int e = 0; e < kRun; ++e) atomicAdd(&sh.hist[bin_of(x[e])], 1);
-  });
-  __syncthreads();
-  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin, &sh.above);
-  __syncthreads();
-  const uint32_t B = static_cast<uint32_t>(min(max(sh.bin, 0), kBins - 1));
-  const int need0 = k - sh.above;
-
-  runs([&](const float* x, int, int nv) {
-    uint32_t cmask = 0;
-#pragma unroll
-    for (int e = 0; e < kRun; ++e) cmask |= static_cast<uint32_t>((bin_of(x[e]) == B) & (e < nv)) << e;
-    const int cnt = __popc(cmask);
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int base = 0;
-    if (lane == 63 && incl > 0) base = atomicAdd(&sh.cnt, incl);
-    base = __shfl(base, 63) + incl - cnt;
-    if (cmask) {
-#pragma unroll
-      for (int e = 0; e < kRun; ++e) {
-        if ((cmask >> e) & 1u) {
-          if (base < kCand) sh.cand[base] = fkey(x[e]);
-          ++base;
-        }
-      }
-    }
-  });
-  __syncthreads();
-
-  exact_threshold(sh, need0, [&](auto f) {
-    runs([&](const float* x, int, int nv) {
-#pragma unroll
-      for (int e = 0; e < kRun; ++e)
-        if (e < nv && bin_of(x[e]) == B) f(x[e]);
-    });
-  });
-  const float tau = key_to_float(sh.tau);
-  const int need = sh.need;
-
-  int base_gt = 0, base_eq = 0;
-  runs([&](const float* x, int i0, int nv) {
-    uint32_t gmask = 0, emask = 0;
-#pragma unroll
-    for (int e = 0; e < kRun; ++e) {
-      gmask |= static_cast<uint32_t>(x[e] > tau) << e;
-      emask |= static_cast<uint32_t>((x[e] == tau) & (e < nv)) << e;
-    }
-    const int gt = __popc(gmask), eq = __popc(emask);
-    int tot;
-    const int ex = block_excl_scan(gt | (eq << 16), sh.wsum, &tot);
-    const int eq_before = base_eq + (ex >> 16);
-    int take = need - eq_before;
-    take = take < 0 ? 0 : (take > eq ? eq : take);
-    if (gt + take > 0) {
-      int pos = base_gt + (ex & 0xffff) + min(need, eq_before);
-      uint32_t keep = emask;
-      for (int drop = eq - take; drop > 0; --drop) keep &= ~(0x80000000u >> __clz(keep));
-      const uint32_t pick = gmask | keep;
-#pragma unroll
-      for (int e = 0; e < kRun; ++e) {
-        if ((pick >> e) & 1u) {
-          if (pos < k) out[pos] = i0 + e;
-          ++pos;
-        }
-      }
-    }
-    base_gt += tot & 0xffff;
-    base_eq += tot >> 16;
-  });
+// Tile elements per thread of the split path for rows of n scores.
+int split_items(int n) { return n <= 65536 ? 4 : 8; }
+int split_slices(int n) {
+  const int tile = kTopkThreads * split_items(n);
+  return (n + tile - 1) / tile;
+}
+// The split path serves rows longer than 16K scores, and rows of more than 4K
+// when they are too few to fill the chip one per CU.
+bool split_shape(int rows, int n) {
+  return n > 16 * kTopkThreads || (n > 4 * kTopkThreads && rows < 128);
 }
 
 }  // namespace
 
-hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
-                       int ld_idx, hipStream_t st) {
-  if (rows == 0 || n == 0) return hipSuccess;
-  const dim3 grid(rows), block(kTopkThreads);
+size_t topk_workspace_bytes(int rows, int n) {
+  if (rows <= 0 || n <= 0 || !split_shape(rows, n)) return 0;
+  const size_t tiles = static_cast<size_t>(rows) * split_slices(n);
+  return tiles * (2 * kBins * sizeof(int) + kTopkThreads * split_items(n) * sizeof(uint2));
+}
+
+int topk_max_row() { return kMaxSlices * kTopkThreads * 8; }
+
+template <bool VEC>
+void launch_rows(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
+                 int ld_idx, void* ws, hipStream_t st) {
+  const dim3 block(kTopkThreads);
+  if (k < n && split_shape(rows, n)) {
+    const int slices = split_slices(n);
+    const dim3 grid(rows * slices);
+    int* part = static_cast<int*>(ws);
+    if (split_items(n) == 4) {
+      hipLaunchKernelGGL((topk_hist_kernel<4, VEC>), grid, block, 0, st, scores, n, ld_scores, slices, part);
+      hipLaunchKernelGGL((topk_split_kernel<4, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices, part, idx, ld_idx);
+    } else {
+      hipLaunchKernelGGL((topk_hist_kernel<8, VEC>), grid, block, 0, st, scores, n, ld_scores, slices, part);
+      hipLaunchKernelGGL((topk_split_kernel<8, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices, part, idx, ld_idx);
+    }
+    return;
+  }
+  const dim3 grid(rows);
   if (n <= 4 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg_kernel<4>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+    hipLaunchKernelGGL((topk_reg_kernel<4, VEC>), grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
   else if (n <= 8 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+    hipLaunchKernelGGL((topk_reg_kernel<8, VEC>), grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
   else if (n <= 16 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg_kernel<16>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
-  else if (n <= 32 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg_kernel<32>, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
-  else
-    hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+    hipLaunchKernelGGL((topk_reg_kernel<16, VEC>), grid, block, 0, st, scores, n, k, ld_scores, idx, ld_idx);
+  else  // k >= n
+    hipLaunchKernelGGL(topk_all_kernel, dim3(min((n + 255) / 256, 64), rows), dim3(256), 0, st, n, idx,
+                       ld_idx);
+}
+
+hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
+                       int ld_idx, void* ws, hipStream_t st) {
+  if (rows == 0 || n == 0) return hipSuccess;
+  // 16-byte loads need aligned rows and whole groups of four
+  const bool vec = (ld_scores % 4 == 0) && (n % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  if (vec) launch_rows<true>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, st);
+  else launch_rows<false>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, st);
   return hipGetLastError();
 }
 

@@ -116,6 +116,12 @@ def test_topk_rejects():
     assert lib.qk_topk(-1, 100, 10, _p(), 100, _p(), 10, None, 0, None) == SHAPE
     assert lib.qk_topk(4, 100, 10, None, 100, _p(), 10, None, 0, None) == NULL
     assert lib.qk_topk(4, 100, 10, _p(FAKE + 2), 100, _p(), 10, None, 0, None) == ALIGN
+    # few long rows are split over workgroups and need scratch
+    need = qk.topk_workspace_bytes(8, 32768)
+    assert lib.qk_topk(8, 32768, 10, _p(), 32768, _p(), 10, None, need, None) == NULL
+    assert lib.qk_topk(8, 32768, 10, _p(), 32768, _p(), 10, _p(), need - 1, None) == WS
+    assert lib.qk_topk(8, 32768, 10, _p(), 32768, _p(), 10, _p(FAKE + 4), need, None) == ALIGN
+    assert lib.qk_topk(1, 8388609, 10, _p(), 8388609, _p(), 10, _p(), 1 << 40, None) == UNSUP
     # nothing to do is not an error
     assert lib.qk_topk(0, 100, 10, None, 100, None, 10, None, 0, None) == OK
     assert lib.qk_topk(3, 0, 10, None, 0, None, 0, None, 0, None) == OK
@@ -164,3 +170,13 @@ def test_workspace_sizes():
                                  "sparse_attn") == 0
     bad = qk.Shape(1, 7, 2, 128, 256, 32768, 33024, 32, 8192)
     assert qk.qk_workspace_bytes(bad, "sparse_attn") == 0
+    # top-k of a split row, per tile: a 2048-bin histogram and its prefix
+    # (ints), and the tile's (key, position) pairs
+    def tiles(t, size):
+        return t * (2 * 2048 * 4 + size * 8)
+    assert qk.topk_workspace_bytes(8, 32768) == tiles(8 * 8, 4096)
+    assert qk.topk_workspace_bytes(8, 131072) == tiles(8 * 16, 8192)
+    assert qk.topk_workspace_bytes(1, 300001) == tiles(37, 8192)
+    assert qk.topk_workspace_bytes(512, 16384) == 0                    # one workgroup per row
+    assert qk.topk_workspace_bytes(512, 16388) == tiles(512 * 5, 4096)
+    assert qk.topk_workspace_bytes(8, 4096) == 0

@@ -382,9 +382,8 @@ def test_topk_edge_cases(gpu):
     _topk_check(qk, rng.standard_normal((3, 1)).astype(np.float32), 1)
     _topk_check(qk, rng.standard_normal((3, 333)).astype(np.float32), 1, ld_idx=5)
     _topk_check(qk, rng.uniform(-1, 1, (2, 131072)).astype(np.float32), 16384)
-    # rows whose sampled elements (index blocks 4j * 1024 .. + 1023 of each
-    # 32K tile) look nothing like the rest: the sample's band misses and the
-    # full histogram takes over
+    # rows whose 1K blocks alternate between two very different levels: the
+    # per-tile histograms of a split row differ widely
     x = rng.standard_normal((3, 32768)).astype(np.float32)
     blk = (np.arange(32768) // 1024) % 4 == 0
     x[:, blk] += 5.0
@@ -393,6 +392,35 @@ def test_topk_edge_cases(gpu):
     x = rng.standard_normal((2, 20000)).astype(np.float32)  # partial tile
     x[:, ((np.arange(20000) // 1024) % 4) == 0] -= 4.0
     _topk_check(qk, x, 5000)
+
+
+def test_topk_split_rows(gpu):
+    """Rows spread over several workgroups (few rows longer than 4K scores, or
+    rows longer than 32K): tiles of 4 and 8 elements per thread,
+    ragged last tiles, k at both ends, and boundary bins too large for LDS
+    (many copies of one value), where the candidates are re-read from the row."""
+    qk = gpu
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((6, 12289)).astype(np.float32)
+    for k in (1, 2, 4096, 12288):
+        _topk_check(qk, x, k)
+    _topk_check(qk, rng.standard_normal((100, 5000)).astype(np.float32), 1234)
+    _topk_check(qk, rng.standard_normal((130, 16900)).astype(np.float32), 4000)   # many long rows
+    _topk_check(qk, rng.standard_normal((1, 300001)).astype(np.float32), 70001)      # 37 tiles
+    _topk_check(qk, rng.standard_normal((2, 70000)).astype(np.float32), 30000)       # 8 per thread
+    # one value held by most of the row: its bin overflows the LDS list
+    x = np.full((2, 40000), 0.25, np.float32)
+    x[:, ::7] = rng.standard_normal((2, len(range(0, 40000, 7)))).astype(np.float32)
+    _topk_check(qk, x, 9000)
+    _topk_check(qk, np.zeros((3, 9000), np.float32), 4500)                            # all equal
+    # many near-equal values: one level-1 bin, distinct low bits
+    x = (1.0 + rng.integers(0, 1 << 12, (2, 30000)) * 2.0 ** -20).astype(np.float32)
+    _topk_check(qk, x, 10000)
+    # -0.0 and +0.0 interleaved in a split row
+    z = np.zeros((2, 8192), np.float32)
+    z[:, ::3] = -0.0
+    z[:, 5::11] = 1.0
+    _topk_check(qk, z, 2000)
     # skewed, ragged and extreme k
     _topk_check(qk, rng.exponential(1.0, (3, 32768)).astype(np.float32), 8192)
     _topk_check(qk, rng.standard_normal((2, 12345)).astype(np.float32), 1)
