@@ -311,9 +311,17 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(ScoreCall c) {
   c.s_agg[static_cast<size_t>(bj) * c.t_past + t] = m / fmaxf(sqrtf(n2), kEps);
 }
 
+template <int D, int NQB, int STAGES>
+void launch_grid(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  const dim3 block(64 * kScoreWaves);
+  if (a.q_group)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true>), grid, block, 0, st, a);
+}
+
 template <int D, int NQB>
 void launch_bf16(const ScoreCall& c, hipStream_t st) {
-  constexpr int STAGES = 4;
   const int bnkv = c.b * c.nkv;
   ScoreArgs a;
   a.q_group = c.q_group;
@@ -337,11 +345,12 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   if (bpw > a.blocks_per_bj) bpw = a.blocks_per_bj;
   const long long waves_per_bj = (a.blocks_per_bj + bpw - 1) / bpw;
   a.wgs_per_bj = static_cast<int>((waves_per_bj + kScoreWaves - 1) / kScoreWaves);
-  const dim3 grid(a.wgs_per_bj * bnkv), block(64 * kScoreWaves);
-  if (c.q_group)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true>), grid, block, 0, st, a);
+  const dim3 grid(a.wgs_per_bj * bnkv);
+  // Blocks kept in flight per wave.  A wave with few blocks to score (short
+  // rows) does better with a shallower ring (measured at d = 128: 3 for up to
+  // 4 blocks per wave, 4 beyond).
+  if (D == 128 && NQB == 1 && bpw <= 4) launch_grid<D, NQB, 3>(a, grid, st);
+  else launch_grid<D, NQB, 4>(a, grid, st);
 }
 
 }  // namespace

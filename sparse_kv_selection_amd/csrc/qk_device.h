@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace qk {
 
@@ -70,6 +71,39 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return static_cast<uint32_t>(v);
 }
+// Sum over each aligned group of W consecutive lanes (W a power of two up to
+// 64); every lane gets its group's sum.  Within 16 lanes the partners come
+// from DPP (lane xor 1, xor 2, then the mirrored lane of the 8- and the
+// 16-lane half, which after the earlier steps holds the other half's sum);
+// wider groups add cross-row shuffles.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int W, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+  auto step = [](T x, auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    if constexpr (sizeof(T) == 4 && __is_same(T, float)) return dpp_f<C>(x);
+    else return static_cast<T>(dpp_i<C>(static_cast<int>(x)));
+  };
+  using q1 = std::integral_constant<int, 0xb1>;   // quad_perm [1,0,3,2]
+  using q2 = std::integral_constant<int, 0x4e>;   // quad_perm [2,3,0,1]
+  using hm = std::integral_constant<int, 0x141>;  // row_half_mirror
+  using rm = std::integral_constant<int, 0x140>;  // row_mirror
+  if constexpr (W >= 2) v += step(v, q1{});
+  if constexpr (W >= 4) v += step(v, q2{});
+  if constexpr (W >= 8) v += step(v, hm{});
+  if constexpr (W >= 16) v += step(v, rm{});
+  if constexpr (W >= 32) v += __shfl_xor(v, 16);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
 // Value of lane 63 (for an inclusive scan: the wave total), uniform.
 __device__ __forceinline__ uint32_t lane63(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));

@@ -132,9 +132,10 @@ __device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_
   // SEGMAX == 0 (long chunks): the keys are read from LDS for every comparison
   uint64_t kc[SEGMAX > 0 ? SEGMAX : 1];
 #pragma unroll
-  for (int e = 0; e < SEGMAX; ++e) {
+  for (int e = 0; e < SEGMAX; ++e) {  // reads clamped into the chunk, so the fill is branch-free
     const int j = part * seg + e;
-    kc[e] = (e < seg && j < bcp) ? key(j) : 0ull;  // 0 is below every real key
+    const uint64_t kj = key(min(j, bcp - 1));
+    kc[e] = (e < seg && j < bcp) ? kj : 0ull;  // 0 is below every real key
   }
   for (int i0 = 0; i0 < bcp; i0 += SLOTS) {  // uniform trip count (shuffles below)
     const int i = i0 + slot;
@@ -146,8 +147,7 @@ __device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_
     } else {
       for (int j = part * seg; j < min(part * seg + seg, bcp); ++j) rank += key(j) > ki;
     }
-#pragma unroll
-    for (int o = 1; o < TPP; o <<= 1) rank += __shfl_xor(rank, o);
+    rank = group_sum<TPP>(rank);
     if (part == 0 && i < bcp && rank < nq_keep) out[rank] = i;
   }
 }
@@ -178,17 +178,15 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (RPT > 0) {
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = u * NRL + rl;
-      if (i < bcp) rows[u].load(qh + static_cast<size_t>(i) * D + 8 * c);
-      else rows[u].zero();
-    }
+    for (int u = 0; u < RPT; ++u)  // rows past the chunk re-read its last row (branch-free)
+      rows[u].load(qh + static_cast<size_t>(min(u * NRL + rl, bcp - 1)) * D + 8 * c);
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
+      const bool ok = u * NRL + rl < bcp;
       float x[8];
       rows[u].get(x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      for (int e = 0; e < 8; ++e) acc[e] += ok ? x[e] : 0.f;
     }
   } else {
     for (int i = rl; i < bcp; i += NRL) {
@@ -207,8 +205,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   for (int col = tid / S; col < D; col += NT / S) {
     float sum = 0.f;
     for (int r = tid % S; r < NRL; r += S) sum += part[r * D + col];
-#pragma unroll
-    for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o);
+    sum = group_sum<S>(sum);
     if (tid % S == 0) mq[col] = sum / static_cast<float>(bcp);
   }
   __syncthreads();
@@ -229,11 +226,8 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
     float dot = 0.f, n2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { dot += x[e] * m8[e]; n2 += x[e] * x[e]; }
-#pragma unroll
-    for (int o = CH / 2; o > 0; o >>= 1) {
-      dot += __shfl_xor(dot, o);
-      n2 += __shfl_xor(n2, o);
-    }
+    dot = group_sum<CH>(dot);
+    n2 = group_sum<CH>(n2);
     if (c == 0 && i < bcp) {
       const float sc = -dot / (fmaxf(sqrtf(n2), kEps) * mq_norm);
       sq[i] = sc;
