@@ -84,29 +84,76 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
 }
-template <int W, typename T>
-__device__ __forceinline__ T group_sum(T v) {
+template <int W, typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, Op op) {
   auto step = [](T x, auto ctrl) {
     constexpr int C = decltype(ctrl)::value;
-    if constexpr (sizeof(T) == 4 && __is_same(T, float)) return dpp_f<C>(x);
+    if constexpr (__is_same(T, float)) return dpp_f<C>(x);
     else return static_cast<T>(dpp_i<C>(static_cast<int>(x)));
   };
   using q1 = std::integral_constant<int, 0xb1>;   // quad_perm [1,0,3,2]
   using q2 = std::integral_constant<int, 0x4e>;   // quad_perm [2,3,0,1]
   using hm = std::integral_constant<int, 0x141>;  // row_half_mirror
   using rm = std::integral_constant<int, 0x140>;  // row_mirror
-  if constexpr (W >= 2) v += step(v, q1{});
-  if constexpr (W >= 4) v += step(v, q2{});
-  if constexpr (W >= 8) v += step(v, hm{});
-  if constexpr (W >= 16) v += step(v, rm{});
-  if constexpr (W >= 32) v += __shfl_xor(v, 16);
-  if constexpr (W >= 64) v += __shfl_xor(v, 32);
+  if constexpr (W >= 2) v = op(v, step(v, q1{}));
+  if constexpr (W >= 4) v = op(v, step(v, q2{}));
+  if constexpr (W >= 8) v = op(v, step(v, hm{}));
+  if constexpr (W >= 16) v = op(v, step(v, rm{}));
+  if constexpr (W >= 32) v = op(v, __shfl_xor(v, 16));
+  if constexpr (W >= 64) v = op(v, __shfl_xor(v, 32));
   return v;
+}
+template <int W, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+  return group_reduce<W>(v, [](T a, T b) { return a + b; });
 }
 
 // Value of lane 63 (for an inclusive scan: the wave total), uniform.
 __device__ __forceinline__ uint32_t lane63(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// Histograms in LDS carry one padding word per 32 bins, so that the lanes of
+// a crossing search, each reading a run of consecutive bins, hit different
+// banks.  hpad(b) is the word of bin b.
+__device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
+__host__ __device__ constexpr int hist_words(int bins) { return bins + bins / 32; }
+
+// Called by one whole wave: the bin b of counts h[hpad(0 .. 64 * PER)) with
+// count(bins > b) < need <= count(bins >= b), for 1 <= need <= total;
+// writes (*bin, *above = count(bins > b)) from the lane that holds it.  Each
+// lane keeps its PER bins in registers: one batch of LDS reads, one wave scan
+// and a register walk.
+template <int PER>
+__device__ void wave_crossing(const int* h, int need, int* bin, int* above) {
+  const int lane = threadIdx.x & 63;
+  const int top = 64 * PER - 1 - lane * PER;  // lane 0 holds the highest bins
+  int c[PER];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    c[q] = h[hpad(top - q)];
+    sum += c[q];
+  }
+  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(sum)));
+  const int ex = incl - sum;
+  if (ex < need && need <= incl) {
+    int b = top, a = ex;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (a + c[q] >= need) { b = top - q; break; }
+      a += c[q];
+    }
+    *bin = b;
+    *above = a;
+  }
+}
+
+// Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -16,6 +16,8 @@
 //      head, slot n): the n-th kept query of each of the G heads is normalised
 //      and the G unit vectors are averaged in a fixed order.  The scoring pass
 //      can form the same means itself from the kept positions instead.
+#include <algorithm>
+
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -46,12 +48,7 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void zero() { a = f32x4{}; b = f32x4{}; }
 };
 
-// Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
-__device__ __forceinline__ uint32_t okey(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+__device__ __forceinline__ uint32_t okey(float x) { return order_key(x); }
 
 // One wave sorts P = 64 * E packed keys descending (bitonic network); lane l
 // holds positions [l * E, (l + 1) * E).  Key = (score key << 32) | ~position,
@@ -112,51 +109,96 @@ __device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* ou
   }
 }
 
-// Top-NQ positions by rank.  With key(i) = (order-preserving SQ key << 32) |
-// ~i, the rank of position i is the number of keys larger than key(i) (larger
-// score, or equal score at a lower position): unique ranks that order the kept
-// queries by decreasing SQ, ties to the lower position.  16 consecutive
-// threads share a position; thread p of the group caches the keys of segment p
-// in registers (SEGMAX >= bcp / 16; 0: read from LDS instead), so every
-// comparison is one 64-bit compare,
-// and the 16 partial counts meet by shuffles.
-template <int NT, int SEGMAX>
-__device__ void top_positions_rank(const float* sq, int bcp, int nq_keep, int32_t* out) {
-  constexpr int TPP = 16;
-  constexpr int SLOTS = NT / TPP;
-  const int part = threadIdx.x % TPP, slot = threadIdx.x / TPP;
-  const int seg = (bcp + TPP - 1) / TPP;
+// Top-NQ positions of sq[0..bcp) by decreasing key K(i) = (order key of
+// sq[i] << 32) | ~i: larger scores first, equal scores at the lower position
+// first (keys are unique, so the result is exact and deterministic).
+//   1. histogram over 2048 equal-width bins between the smallest and the
+//      largest score (the bin is monotone in the score); the boundary bin B
+//      holds the NQ-th largest key, `above` keys lie in higher bins;
+//   2. the positions of the higher bins (list A, fewer than NQ) and of bin B
+//      (list C) are appended to LDS;
+//   3. each entry of A is ranked among A and each of C among C by counting
+//      larger keys, 16 threads per entry; A's ranks are final, C's are offset
+//      by |A| and kept while below NQ - |A|.
+// scratch: hist_words(2048) + 256 + bcp + 4 ints.  Every thread of the block
+// calls this.
+template <int NT>
+__device__ void top_positions_select(const float* sq, int* scratch, int bcp, int nq_keep,
+                                     int32_t* out) {
+  constexpr int kB = 2048, kWaves = NT / 64, TPP = 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* hist = scratch;
+  int* la = hist + hist_words(kB);
+  int* lc = la + 256;
+  int* cnt = lc + bcp;  // |A|, |C|, B, above
+  __shared__ float red[2][kWaves];
   auto key = [&](int i) {
     return (static_cast<uint64_t>(okey(sq[i])) << 32) | static_cast<uint32_t>(~i);
   };
-  // SEGMAX == 0 (long chunks): the keys are read from LDS for every comparison
-  uint64_t kc[SEGMAX > 0 ? SEGMAX : 1];
-#pragma unroll
-  for (int e = 0; e < SEGMAX; ++e) {  // reads clamped into the chunk, so the fill is branch-free
-    const int j = part * seg + e;
-    const uint64_t kj = key(min(j, bcp - 1));
-    kc[e] = (e < seg && j < bcp) ? kj : 0ull;  // 0 is below every real key
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < bcp; i += NT) {
+    mn = fminf(mn, sq[i]);
+    mx = fmaxf(mx, sq[i]);
   }
-  for (int i0 = 0; i0 < bcp; i0 += SLOTS) {  // uniform trip count (shuffles below)
-    const int i = i0 + slot;
-    const uint64_t ki = key(min(i, bcp - 1));
-    int rank = 0;
-    if constexpr (SEGMAX > 0) {
+  mn = group_reduce<64>(mn, [](float a, float b) { return fminf(a, b); });
+  mx = group_reduce<64>(mx, [](float a, float b) { return fmaxf(a, b); });
+  if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
+  for (int i = tid; i < hist_words(kB); i += NT) hist[i] = 0;
+  if (tid < 2) cnt[tid] = 0;
+  __syncthreads();
 #pragma unroll
-      for (int e = 0; e < SEGMAX; ++e) rank += kc[e] > ki;
-    } else {
-      for (int j = part * seg; j < min(part * seg + seg, bcp); ++j) rank += key(j) > ki;
+  for (int w = 0; w < kWaves; ++w) { mn = fminf(mn, red[0][w]); mx = fmaxf(mx, red[1][w]); }
+  float scale = static_cast<float>(kB) / (mx - mn);
+  if (!(scale < INFINITY)) scale = 0.f;  // all scores equal: one bin
+  auto bin = [&](int i) { return min(max(static_cast<int>((sq[i] - mn) * scale), 0), kB - 1); };
+  for (int i = tid; i < bcp; i += NT) atomicAdd(&hist[hpad(bin(i))], 1);
+  __syncthreads();
+  if (wave == 0) wave_crossing<kB / 64>(hist, nq_keep, &cnt[2], &cnt[3]);
+  __syncthreads();
+  const int B = cnt[2];
+  for (int i0 = 0; i0 < bcp; i0 += NT) {  // uniform trip count (wave scans below)
+    const int i = i0 + tid;
+    const int bi = i < bcp ? bin(i) : -1;
+    const bool in_a = bi > B, in_c = bi == B;
+    const uint32_t flag = static_cast<uint32_t>(in_a) | (static_cast<uint32_t>(in_c) << 16);
+    const uint32_t incl = wave_incl_scan(flag);
+    uint32_t base = 0;
+    if (lane == 63) {
+      const int na = static_cast<int>(incl & 0xffffu), nc = static_cast<int>(incl >> 16);
+      base = static_cast<uint32_t>(na > 0 ? atomicAdd(&cnt[0], na) : 0) |
+             (static_cast<uint32_t>(nc > 0 ? atomicAdd(&cnt[1], nc) : 0) << 16);
     }
-    rank = group_sum<TPP>(rank);
-    if (part == 0 && i < bcp && rank < nq_keep) out[rank] = i;
+    base = lane63(base);
+    const uint32_t ex = incl - flag;
+    if (in_a) la[(base & 0xffffu) + (ex & 0xffffu)] = i;
+    if (in_c) lc[(base >> 16) + (ex >> 16)] = i;
+  }
+  __syncthreads();
+  const int na = cnt[0], nc = cnt[1], need = nq_keep - cnt[3];
+  const int part = tid % TPP, slot = tid / TPP;
+  for (int t0 = 0; t0 < na + nc; t0 += NT / TPP) {  // uniform trip count (group sums)
+    const int t = t0 + slot;
+    const bool a = t < na;
+    const int* list = a ? la : lc;
+    const int n = t < na + nc ? (a ? na : nc) : 0;
+    const int i = n > 0 ? list[a ? t : t - na] : 0;
+    const uint64_t ki = key(i);
+    int r = 0;
+    for (int j = part; j < n; j += TPP) r += key(list[j]) > ki;
+    r = group_sum<TPP>(r);
+    if (part == 0 && n > 0) {
+      if (a) out[r] = i;
+      else if (r < need) out[na + r] = i;
+    }
   }
 }
 
 // One workgroup of NT threads per query head.  Thread (row lane r, chunk c)
 // owns the 8-element chunk c of rows r, r + NT / CH, ...; RPT > 0: all of
 // them held in registers (one memory trip); RPT == 0: two passes over memory.
-// E > 0: wave 0 sorts 64 * E >= bcp keys; E == 0: rank count instead.
-template <typename T, int D, int NT, int RPT, int E, int SEGMAX>
+// E > 0: wave 0 sorts 64 * E >= bcp keys; E == 0: histogram selection
+// (its scratch reuses the column-sum partials).
+template <typename T, int D, int NT, int RPT, int E>
 __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
                                                        int32_t* __restrict__ q_idx,
                                                        float* __restrict__ sq_out, int bcp,
@@ -165,10 +207,9 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   constexpr int NRL = NT / CH;       // rows handled at once
   constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
   extern __shared__ float smem[];
-  float* part = smem;                // [NRL][D]
-  float* mq = part + NRL * D;        // [D]
+  float* part = smem;                // [NRL][D] (or the selection scratch, if larger)
+  float* mq = part + (E > 0 ? NRL * D : max(NRL * D, hist_words(2048) + 256 + bcp + 4));  // [D]
   float* sq = mq + D;                // [bcp]
-  __shared__ float s_mq2;
   const int tid = threadIdx.x;
   const int c = tid % CH, rl = tid / CH;
   const int bh = blockIdx.x;
@@ -209,17 +250,14 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
     if (tid % S == 0) mq[col] = sum / static_cast<float>(bcp);
   }
   __syncthreads();
-  if (tid < 64) {
-    float m2 = 0.f;
-    for (int e = tid; e < D; e += 64) m2 += mq[e] * mq[e];
-    m2 = wave_sum(m2);
-    if (tid == 0) s_mq2 = m2;
-  }
-  __syncthreads();
-  const float mq_norm = fmaxf(sqrtf(s_mq2), kEps);
-  float m8[8];
+  // |MQ|: the CH lanes of a row group hold all of MQ between them
+  float m8[8], m2 = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m8[e] = mq[8 * c + e];
+  for (int e = 0; e < 8; ++e) {
+    m8[e] = mq[8 * c + e];
+    m2 += m8[e] * m8[e];
+  }
+  const float mq_norm = fmaxf(sqrtf(group_sum<CH>(m2)), kEps);
 
   // SQ per row: the CH lanes of a row sit in one wave
   auto score_row = [&](int i, const float* x) {
@@ -258,7 +296,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   if constexpr (E > 0) {
     if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out);
   } else {
-    top_positions_rank<NT, SEGMAX>(sq, bcp, nq_keep, out);
+    top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out);
   }
 }
 
@@ -312,19 +350,17 @@ template <typename T, int D, int NT, int RPT>
 void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bcp, int nq_keep,
                  hipStream_t st) {
   constexpr int NRL = NT / (D / 8);
-  const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
   const dim3 grid(b * nq), block(NT);
   const T* qq = static_cast<const T*>(q);
-  // up to 64 positions: one-wave sort; beyond: rank counting over the block
-  // with bcp / 16 keys cached per thread
-  if (bcp <= 64)
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
-  else if (bcp <= 256)
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 16>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
-  else if (bcp <= 512)
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 32>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
-  else
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  // up to 64 positions: one-wave sort; beyond: histogram selection
+  if (bcp <= 64) {
+    const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  } else {
+    const size_t part = std::max<size_t>(static_cast<size_t>(NRL) * D, hist_words(2048) + 256 + bcp + 4);
+    const size_t shm = sizeof(float) * (part + D + bcp);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+  }
 }
 
 template <typename T, int D>

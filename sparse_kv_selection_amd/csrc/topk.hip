@@ -36,21 +36,12 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 4096;  // boundary-bin candidates kept in LDS
 
-// Order-preserving map of a float to uint32 (-0.0 maps like +0.0).
-__device__ __forceinline__ uint32_t fkey(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+__device__ __forceinline__ uint32_t fkey(float x) { return order_key(x); }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Histograms are stored with one padding word per 32 bins, so that the lanes
-// of the crossing search, each reading a run of consecutive bins, hit
-// different LDS banks.
-constexpr int kHistWords = kBins + kBins / 32;
-__device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
+constexpr int kHistWords = hist_words(kBins);
 
 struct TopkShared {
   int hist[kHistWords];
@@ -60,35 +51,6 @@ struct TopkShared {
   int bin, above, cnt, need;
   uint32_t tau;
 };
-
-// Wave 0 only: the bin b of counts h[hpad(0 .. 64 * PER)) with
-// count(bins > b) < need <= count(bins >= b); writes (*bin, *above) from the
-// lane that holds it.  Each lane keeps its PER bins in registers, so the search
-// is one batch of LDS reads, one wave scan and a register walk.
-template <int PER>
-__device__ void wave_crossing(const int* h, int need, int* bin, int* above) {
-  const int lane = threadIdx.x & 63;
-  const int top = 64 * PER - 1 - lane * PER;  // lane 0 holds the highest bins
-  int c[PER];
-  int sum = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    c[q] = h[hpad(top - q)];
-    sum += c[q];
-  }
-  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(sum)));
-  const int ex = incl - sum;
-  if (ex < need && need <= incl) {
-    int b = top, a = ex;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      if (a + c[q] >= need) { b = top - q; break; }
-      a += c[q];
-    }
-    *bin = b;
-    *above = a;
-  }
-}
 
 // Exact threshold among the LDS candidate list: the need-th largest key.
 // Writes sh.tau and sh.need (copies of the threshold still to take).
