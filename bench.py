@@ -36,13 +36,14 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
 # the plain-copy calibration (2 x FETCH_SIZE + 1 x WRITE_SIZE, KiB -> bytes),
 # keyed by (workload, stage) and valid only for the kernel source they were
-# taken on (first 16 hex digits of the source file's SHA-256): once the source
-# changes, the figure no longer describes the kernel and `traffic` is null.
+# taken on (first 16 hex digits of the SHA-256 of the kernel's source file
+# followed by the shared device header): once either changes, the figure no
+# longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "7931e1a45779160a", 69358633),
-    ("llama3b_32k", "attention"): ("attention.hip", "97f0ffe1fe36e8d7", 68401629 + 35107741),
-    ("long_128k", "kvscore"): ("kvscore.hip", "7931e1a45779160a", 273813205),
-    ("long_128k", "attention"): ("attention.hip", "97f0ffe1fe36e8d7", 112123112 + 44364563),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 69912572),
+    ("llama3b_32k", "attention"): ("attention.hip", "5ff1260fd71c64d6", 74434489),
+    ("long_128k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 277117628),
+    ("long_128k", "attention"): ("attention.hip", "5ff1260fd71c64d6", 124265450),
 }
 
 
@@ -52,9 +53,12 @@ def measured_traffic(workload: str, stage: str):
     if entry is None:
         return None
     fname, digest, nbytes = entry
-    path = os.path.join(ROOT, "sparse_kv_selection_amd", "csrc", fname)
-    with open(path, "rb") as f:
-        current = hashlib.sha256(f.read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "sparse_kv_selection_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (fname, "qk_device.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    current = h.hexdigest()[:16]
     return nbytes if current == digest else None
 
 
@@ -212,31 +216,41 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-stage durations on the same stream (events between the calls)
+    # Per-stage kernel time: each stage is launched `reps` times back to back
+    # over the rotating input copies, between two events on the current stream
+    # (the launches are enqueued ahead, so host gaps between calls do not
+    # count).  A stage reads the previous stage's outputs as they stand, which
+    # are valid inputs of the same shape.
     stages = ["qsel", "kvscore", "select", "attention"]
-    acc = {s: 0.0 for s in stages}
-    reps = max(10, args.steps)
-    for i in range(reps):
-        c = inputs[i % copies]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        ev[0].record()
-        qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
-        ev[1].record()
-        qk.qk_kvscore_grouped(shape, c["q"], pipe.q_idx, c["k"], pipe.s_agg)
-        ev[2].record()
-        if rounds:
-            qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"], spec.top_rounds,
-                               True, pipe.idx, pipe.ld_idx, pipe.sel_len, pipe.s_round)
+
+    def run_stage(name, c):
+        if name == "qsel":
+            qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
+        elif name == "kvscore":
+            qk.qk_kvscore_grouped(shape, c["q"], pipe.q_idx, c["k"], pipe.s_agg)
+        elif name == "select":
+            if rounds:
+                qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"],
+                                   spec.top_rounds, True, pipe.idx, pipe.ld_idx, pipe.sel_len,
+                                   pipe.s_round)
+            else:
+                qk.qk_topk(shape.b * shape.nkv, shape.t_past, shape.bsa, pipe.s_agg,
+                           shape.t_past, pipe.idx, pipe.ld_idx, pipe.topk_ws, pipe.topk_ws_bytes)
         else:
-            qk.qk_topk(shape.b * shape.nkv, shape.t_past, shape.bsa, pipe.s_agg, shape.t_past,
-                       pipe.idx, pipe.ld_idx, pipe.topk_ws, pipe.topk_ws_bytes)
-        ev[3].record()
-        pipe.attend(c["q"], c["k"], c["v"])
-        ev[4].record()
+            pipe.attend(c["q"], c["k"], c["v"])
+
+    reps = max(10, args.steps)
+    stage_ms = {}
+    for sname in stages:
+        for i in range(2):
+            run_stage(sname, inputs[i % copies])
         torch.cuda.synchronize()
-        for si, s in enumerate(stages):
-            acc[s] += ev[si].elapsed_time(ev[si + 1])
-    stage_ms = {s: acc[s] / reps for s in stages}
+        e0.record()
+        for i in range(reps):
+            run_stage(sname, inputs[i % copies])
+        e1.record()
+        torch.cuda.synchronize()
+        stage_ms[sname] = e0.elapsed_time(e1) / reps
 
     n_sel = float(pipe.sel_len.float().mean()) if rounds else float(shape.n_sel)
     work = algorithmic(spec, n_sel)
