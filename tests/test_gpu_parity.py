@@ -153,6 +153,23 @@ def test_kvscore_grouped(gpu, name):
     assert err <= 5e-5, f"precision regression: {err}"
 
 
+def test_kvscore_grouped_unsorted_positions(gpu):
+    """The group means pair slot n of every head whatever the positions are:
+    kept positions given in an arbitrary (unsorted, repeated) order score like
+    the oracle's group queries built from the same lists."""
+    qk = gpu
+    spec, case, ref, g = _case("llama_ragged")
+    s = _shape(spec, qk)
+    rng = np.random.default_rng(31)
+    pos = rng.integers(0, s.bcp, size=(s.b, s.nq, s.nq_keep)).astype(np.int32)
+    qg = oracle.group_queries(np64(case["q"]), pos, s.nkv)
+    s_agg = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    qk.qk_kvscore_grouped(s, g["q"], torch.from_numpy(pos).to(_dev()), g["k"], s_agg)
+    torch.cuda.synchronize()
+    _, want = oracle.key_scores(qg, np64(case["k"]), s.t_past)
+    assert max_abs(s_agg, want) <= 5e-5
+
+
 def test_kvscore_grouped_matches_split_path(gpu):
     """The fused scoring pass and qk_qsel's group means followed by qk_kvscore
     agree (same kept positions), on a case with G = 8 (two position batches)
@@ -392,6 +409,37 @@ def test_topk_edge_cases(gpu):
     x = rng.standard_normal((2, 20000)).astype(np.float32)  # partial tile
     x[:, ((np.arange(20000) // 1024) % 4) == 0] -= 4.0
     _topk_check(qk, x, 5000)
+
+
+def test_topk_workspace_reuse_and_unaligned_rows(gpu):
+    """One top-k workspace serves calls of different shapes (a large split
+    call, a smaller one, the large one again); rows that start 4 bytes off a
+    16-byte boundary take the element-wise load path.  Every result matches the
+    oracle's sort."""
+    qk = gpu
+    rng = np.random.default_rng(29)
+    big = rng.standard_normal((4, 70000)).astype(np.float32)
+    small = rng.standard_normal((9, 20000)).astype(np.float32)
+    nws = max(qk.topk_workspace_bytes(4, 70000), qk.topk_workspace_bytes(9, 20000))
+    ws = torch.full((nws,), 0x7f, dtype=torch.uint8, device=_dev())
+    for x, k in ((big, 17000), (small, 5000), (big, 17000)):
+        rows, n = x.shape
+        idx = torch.full((rows, k), -1, dtype=torch.int32, device=_dev())
+        qk.qk_topk(rows, n, k, torch.from_numpy(x).to(_dev()), n, idx, k, ws, nws)
+        torch.cuda.synchronize()
+        want = oracle.select_keys(x.astype(np.float64)[None], k)[0]
+        assert np.array_equal(npi(idx), want)
+    # rows at an odd element offset (4-byte aligned only), leading dimension n + 1
+    x = rng.standard_normal((3, 9001 * 3 + 1)).astype(np.float32)
+    buf = torch.from_numpy(x.reshape(-1)).to(_dev())
+    rows, n, ld, k = 3, 9000, 9001, 2500
+    view = buf[1:1 + rows * ld]
+    idx = torch.full((rows, k), -1, dtype=torch.int32, device=_dev())
+    qk.qk_topk(rows, n, k, view, ld, idx, k)
+    torch.cuda.synchronize()
+    scores = x.reshape(-1)[1:1 + rows * ld].reshape(rows, ld)[:, :n]
+    want = oracle.select_keys(scores.astype(np.float64)[None], k)[0]
+    assert np.array_equal(npi(idx), want)
 
 
 def test_topk_split_rows(gpu):
