@@ -274,9 +274,6 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
       return as_bf16x8(*reinterpret_cast<const u32x4*>(cK + kb * 32 * D + kofs[s % NKA] +
                                                        128 * (s / NKA)));
     };
-    // the product phase runs at raised wave priority: while this wave feeds the
-    // matrix cores, another resident wave's softmax work fills the gaps
-    __builtin_amdgcn_s_setprio(1);
     bf16x8 ka0 = kfrag(0, 0), ka1 = kfrag(0, 1);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -291,7 +288,6 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
         S[1][nb] = mfma32(c1, qf[nb][s], S[1][nb]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
     const bool is_chunk = t >= npt;
     const int kbase = is_chunk ? (c0 + t - npt) * kKeyTile : (pt0 + t) * kKeyTile;
     if (t >= n_full) {  // uniform: boundary and chunk tiles only
@@ -358,6 +354,11 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
     auto vfrag = [&](int n) {  // key group n / (D / 32), d block n % (D / 32)
       return lds_read_tr_pair(cV + vofs[n % (D / 32)] + (n / (D / 32)) * 16 * D, D);
     };
+    // The value products run at raised wave priority: while this wave feeds
+    // the matrix cores its tile's vector work is done, and the other resident
+    // wave's exponentials fill the gaps (measured: about 3 % faster than
+    // raising it for the key products).
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 va = vfrag(0);
 #pragma unroll
     for (int n = 0; n < D / 8; ++n) {
@@ -367,6 +368,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
       for (int nb = 0; nb < NB; ++nb)
         acc[nb][n % (D / 32)] = mfma32(cur, P[nb][n / (D / 32)], acc[nb][n % (D / 32)]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Tile t lives in stage t & 1.  Iteration t: wait for its loads (own, then
