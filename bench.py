@@ -40,10 +40,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # followed by the shared device header): once either changes, the figure no
 # longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 69912572),
-    ("llama3b_32k", "attention"): ("attention.hip", "5ff1260fd71c64d6", 74434489),
-    ("long_128k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 277117628),
-    ("long_128k", "attention"): ("attention.hip", "5ff1260fd71c64d6", 124265450),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 69912581),
+    ("llama3b_32k", "attention"): ("attention.hip", "91fb786784e34190", 74132441),
+    ("long_128k", "kvscore"): ("kvscore.hip", "7053056cd2789d8c", 277112357),
+    ("long_128k", "attention"): ("attention.hip", "91fb786784e34190", 124266843),
 }
 
 
