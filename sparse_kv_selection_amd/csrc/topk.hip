@@ -320,32 +320,50 @@ __global__ __launch_bounds__(256) void topk_all_kernel(int n, int32_t* __restric
 // Split path for rows that are few or long: one row is spread over `slices`
 // workgroups of 1024 threads, each owning a tile of 1024 * IPT elements.
 //   pass 1 (topk_hist_kernel): each workgroup counting-sorts its tile by the
-//     top 11 bits of the order-preserving key: it writes the tile's histogram,
-//     its exclusive prefix, and the tile's (key, position) pairs grouped by
-//     bin (workspace; nothing needs initialising);
+//     level-1 bin of the order-preserving key (l1_bin below): it writes the
+//     tile's histogram, its exclusive prefix, and the tile's (key, position)
+//     pairs grouped by bin (workspace; nothing needs initialising);
 //   pass 2 (topk_split_kernel): each workgroup sums the row's histograms and
 //     finds the boundary bin B, reads bin B's pairs from every tile's groups
-//     into LDS, fixes the remaining 21 key bits of the k-th largest key with
-//     two more radix levels over them, counts what earlier tiles contribute,
-//     and writes the positions picked in its own tile.
+//     into LDS, finds the k-th largest key among them (each ranked against
+//     the others when they are few, else radix levels over their key range),
+//     counts what earlier tiles contribute, and writes the positions picked
+//     in its own tile.
 // Workspace, for W = rows * slices workgroups: W histograms, W prefixes
 // (2048 ints each), then W tiles of (key, position) pairs.
 // ---------------------------------------------------------------------------
-constexpr int kL1Shift = 21;       // level-1 bin = key >> 21 (2048 bins)
 constexpr int kSplitCand = 6144;   // bin-B pairs kept in LDS
 constexpr int kCandPerThread = kSplitCand / kTopkThreads;
+constexpr int kRankMax = kTopkThreads;  // bin B ranked pair by pair up to this size
+
+// Level-1 bin of an order key (2048 bins), monotone in the key so that every
+// bin above the boundary bin is selected whole.  Each sign gets 1024 bins:
+// 128 per binade of |x| over [2^-8, 2^(1022/128 - 8)) (about 0.0039 to 0.98,
+// where cosine scores lie), one bin for the smaller magnitudes next to zero
+// and one for the larger ones (and NaN) at the end.  The top bits of the key
+// alone would spend most bins on exponents that such scores never reach and
+// put a tenth of a row into one bin.
+constexpr int kFineBase = 119 << 7;  // (exponent, top 7 mantissa bits) of 2^-8
+__device__ __forceinline__ int l1_bin(uint32_t key) {
+  const bool pos = key >= 0x80000000u;
+  const uint32_t mag = pos ? (key & 0x7fffffffu) : (0x7fffffffu - key);  // bits of |x|
+  const int v = static_cast<int>(mag >> 16) - kFineBase;
+  const int i = v < 0 ? 0 : min(v + 1, 1023);
+  return pos ? 1024 + i : 1023 - i;
+}
 
 template <int IPT, bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __restrict__ scores,
                                                                  int n, int ld_scores, int slices,
                                                                  int* __restrict__ part) {
+  constexpr int kTile = kTopkThreads * IPT;
   __shared__ int h[kBins];
   __shared__ int wtot[kTopkWaves];
+  __shared__ uint4 stage[kTile / 2];  // the tile's pairs in bin order, two per entry
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int w = blockIdx.x, nwg = gridDim.x;
   const int row = w / slices, sl = w - row * slices;
   const float* s = scores + static_cast<size_t>(row) * ld_scores;
-  constexpr int kTile = kTopkThreads * IPT;
   for (int i = tid; i < kBins; i += kTopkThreads) h[i] = 0;
   float x[IPT];
   const uint32_t valid = load_tile<IPT, VEC>(s, sl * kTile, n, x);
@@ -355,7 +373,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < IPT; ++e)
-    if ((valid >> e) & 1u) atomicAdd(&h[kx[e] >> kL1Shift], 1);
+    if ((valid >> e) & 1u) atomicAdd(&h[l1_bin(kx[e])], 1);
   __syncthreads();
   // exclusive prefix over the bins; thread t owns bins 2t and 2t + 1
   const int c0 = h[2 * tid], c1 = h[2 * tid + 1];
@@ -371,31 +389,40 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __
   h[2 * tid] = ex;  // now the bins' write cursors (each thread rewrites only its own bins)
   h[2 * tid + 1] = ex + c0;
   __syncthreads();
-  uint2* pairs = reinterpret_cast<uint2*>(part + 2 * static_cast<size_t>(nwg) * kBins) +
-                 static_cast<size_t>(w) * kTile;
+  // The pairs are sorted into LDS and then written out contiguously: with
+  // scores spread over many bins, direct scattered 8-byte stores would each
+  // touch a line of their own.
+  uint2* lp = reinterpret_cast<uint2*>(stage);
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     if ((valid >> e) & 1u) {
-      const int slot = atomicAdd(&h[kx[e] >> kL1Shift], 1);
+      const int slot = atomicAdd(&h[l1_bin(kx[e])], 1);
       if (slot < kTile)  // always: the slots of a bin end where the next bin's begin
-        pairs[slot] = uint2{kx[e], static_cast<uint32_t>(tile_pos<IPT>(sl * kTile, e))};
+        lp[slot] = uint2{kx[e], static_cast<uint32_t>(tile_pos<IPT>(sl * kTile, e))};
     }
   }
+  __syncthreads();
+  uint4* pairs = reinterpret_cast<uint4*>(part + 2 * static_cast<size_t>(nwg) * kBins) +
+                 static_cast<size_t>(w) * (kTile / 2);
+  const int nvalid = min(kTile, n - sl * kTile);  // slots [0, nvalid) are filled
+  for (int i = tid; 2 * i < nvalid; i += kTopkThreads) pairs[i] = stage[i];
 }
 
 constexpr int kMaxSlices = 1024;
 
 struct SplitShared {
   int hist[kHistWords];       // the row's level-1 histogram
-  int hist2[kHistWords];      // bits 20..10 of bin B's keys
-  int hist3[kHistWords / 2];  // bits 9..0
-  uint32_t ckey[kSplitCand];
+  int hist2[kHistWords];      // radix levels over bin B's key range
+  alignas(16) uint32_t ckey[kSplitCand];
   int cpos[kSplitCand];
   int seg_start[kMaxSlices + 1];  // bin B's pairs of tile t: [seg_start[t], seg_start[t + 1])
   int seg_off[kMaxSlices];        // ... found at this offset in tile t's sorted pairs
   uint32_t wsum[kTopkWaves];
   int red[2][kTopkWaves];
-  int bin[3], above[3];
+  uint32_t kred[2][kTopkWaves];
+  int bin[2], above[2];
+  uint32_t tau;
+  int need;
 };
 
 // Sum over the block of (a, b); every thread gets the totals.
@@ -457,8 +484,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
   // 1. boundary bin B of the row; bins above it in earlier tiles
 #pragma unroll
   for (int u = 0; u < U; ++u) sh.hist[hpad(tid + kTopkThreads * u)] = total[u];
-  for (int i = tid; i < kHistWords; i += kTopkThreads) sh.hist2[i] = 0;
-  for (int i = tid; i < kHistWords / 2; i += kTopkThreads) sh.hist3[i] = 0;
   __syncthreads();
   if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin[0], &sh.above[0]);
   __syncthreads();
@@ -527,22 +552,74 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
     }
   };
 
-  // 3. the k-th largest key: bits 20..10, then bits 9..0, from histograms of bin B
-  visit([&](uint32_t kx, int) { atomicAdd(&sh.hist2[hpad((kx >> 10) & 2047u)], 1); });
-  __syncthreads();
-  if (wave == 0) wave_crossing<2048 / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
-  __syncthreads();
-  need -= sh.above[1];
-  const uint32_t prefix = (B << kL1Shift) | (static_cast<uint32_t>(min(max(sh.bin[1], 0), 2047)) << 10);
-  visit([&](uint32_t kx, int) {
-    if ((kx & 0xfffffc00u) == prefix) atomicAdd(&sh.hist3[hpad(kx & 1023u)], 1);
-  });
-  __syncthreads();
-  if (wave == 0) wave_crossing<1024 / 64>(sh.hist3, need, &sh.bin[2], &sh.above[2]);
-  __syncthreads();
-  need -= sh.above[2];
-  const uint32_t tau = prefix | static_cast<uint32_t>(min(max(sh.bin[2], 0), 1023));
-  // tau is the k-th largest key; `need` copies of it are taken (lowest positions first)
+  // 3. the k-th largest key tau of the row, the need-th largest of bin B
+  if (in_lds && nb <= kRankMax) {
+    // few: each candidate counts the greater and equal keys among the others
+    if (tid < nb) {
+      const uint32_t mine = sh.ckey[tid];
+      int gt = 0, eq = 0, c = 0;
+      const uint4* c4 = reinterpret_cast<const uint4*>(sh.ckey);
+      for (; c + 4 <= nb; c += 4) {
+        const uint4 o = c4[c >> 2];
+        gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
+        eq += (o.x == mine) + (o.y == mine) + (o.z == mine) + (o.w == mine);
+      }
+      for (; c < nb; ++c) {
+        const uint32_t o = sh.ckey[c];
+        gt += o > mine;
+        eq += o == mine;
+      }
+      if (gt < need && need <= gt + eq) {  // every holder of this key agrees
+        sh.tau = mine;
+        sh.need = need - gt;
+      }
+    }
+    __syncthreads();
+  } else {
+    // many: radix levels of up to 11 bits over [lo, lo + span], the range
+    // of bin B's keys, until one key is left
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    visit([&](uint32_t kx, int) {
+      kmin = min(kmin, kx);
+      kmax = max(kmax, kx);
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    if (lane == 0) { sh.kred[0][wave] = kmin; sh.kred[1][wave] = kmax; }
+    __syncthreads();
+    uint32_t lo = sh.kred[0][0], hi = sh.kred[1][0];
+#pragma unroll
+    for (int w = 1; w < kTopkWaves; ++w) { lo = min(lo, sh.kred[0][w]); hi = max(hi, sh.kred[1][w]); }
+    uint32_t span = hi - lo;
+    while (span > 0) {  // uniform
+      const int shift = max(0, 21 - __clz(static_cast<int>(span)));  // span >> shift < 2048
+      for (int i = tid; i < kHistWords; i += kTopkThreads) sh.hist2[i] = 0;
+      __syncthreads();
+      visit([&](uint32_t kx, int) {
+        const uint32_t dx = kx - lo;
+        if (kx >= lo && dx <= span) atomicAdd(&sh.hist2[hpad(static_cast<int>(dx >> shift))], 1);
+      });
+      __syncthreads();
+      if (wave == 0) wave_crossing<kBins / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
+      __syncthreads();
+      need -= sh.above[1];
+      const uint32_t dg = static_cast<uint32_t>(min(max(sh.bin[1], 0), kBins - 1)) << shift;
+      lo += dg;
+      span = min(span - dg, (1u << shift) - 1u);
+      __syncthreads();  // bin / above are read before the next level writes them
+    }
+    if (tid == 0) {
+      sh.tau = lo;
+      sh.need = need;
+    }
+    __syncthreads();
+  }
+  const uint32_t tau = sh.tau;
+  need = sh.need;
+  // `need` copies of tau are taken (lowest positions first)
 
   // 4. what earlier tiles contribute: greater keys and copies of tau
   int gt_before = 0, eq_before = 0;

@@ -464,6 +464,13 @@ def test_topk_split_rows(gpu):
     # many near-equal values: one level-1 bin, distinct low bits
     x = (1.0 + rng.integers(0, 1 << 12, (2, 30000)) * 2.0 ** -20).astype(np.float32)
     _topk_check(qk, x, 10000)
+    # a boundary bin of a few thousand near-equal scores inside the cosine range
+    # (more than are ranked pair by pair, few enough for LDS): radix levels
+    x = np.full((2, 20000), -0.5, np.float32)
+    x[:, :3000] = 2.0
+    x[:, 3000:7000] = (0.3 + rng.integers(0, 2048, (2, 4000)) * 2.0 ** -24).astype(np.float32)
+    x = rng.permuted(x, axis=1)
+    _topk_check(qk, x, 5000)
     # -0.0 and +0.0 interleaved in a split row
     z = np.zeros((2, 8192), np.float32)
     z[:, ::3] = -0.0
