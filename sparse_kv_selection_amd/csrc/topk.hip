@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void topk_all_kernel(int n, int32_t* __restric
 // ---------------------------------------------------------------------------
 constexpr int kSplitCand = 6144;   // bin-B pairs kept in LDS
 constexpr int kCandPerThread = kSplitCand / kTopkThreads;
-constexpr int kRankMax = kTopkThreads;  // bin B ranked pair by pair up to this size
+constexpr int kRankDirect = 64;  // bin B ranked pair by pair up to this size
 
 // Level-1 bin of an order key (2048 bins), monotone in the key so that every
 // bin above the boundary bin is selected whole.  Each sign gets 1024 bins:
@@ -350,6 +350,15 @@ __device__ __forceinline__ int l1_bin(uint32_t key) {
   const int v = static_cast<int>(mag >> 16) - kFineBase;
   const int i = v < 0 ? 0 : min(v + 1, 1023);
   return pos ? 1024 + i : 1023 - i;
+}
+// The keys of level-1 bin b: [*lo, *hi].
+__device__ __forceinline__ void l1_bin_range(int b, uint32_t* lo, uint32_t* hi) {
+  const bool pos = b >= 1024;
+  const int i = pos ? b - 1024 : 1023 - b;
+  const uint32_t mlo = i == 0 ? 0u : static_cast<uint32_t>(kFineBase + i - 1) << 16;
+  const uint32_t mhi = i == 1023 ? 0x7fffffffu : (static_cast<uint32_t>(kFineBase + i) << 16) - 1u;
+  *lo = pos ? (0x80000000u | mlo) : (0x7fffffffu - mhi);
+  *hi = pos ? (0x80000000u | mhi) : (0x7fffffffu - mlo);
 }
 
 template <int IPT, bool VEC>
@@ -419,7 +428,6 @@ struct SplitShared {
   int seg_off[kMaxSlices];        // ... found at this offset in tile t's sorted pairs
   uint32_t wsum[kTopkWaves];
   int red[2][kTopkWaves];
-  uint32_t kred[2][kTopkWaves];
   int bin[2], above[2];
   uint32_t tau;
   int need;
@@ -553,18 +561,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
   };
 
   // 3. the k-th largest key tau of the row, the need-th largest of bin B
-  if (in_lds && nb <= kRankMax) {
+  uint32_t tau;
+  if (in_lds && nb <= kRankDirect) {
     // few: each candidate counts the greater and equal keys among the others
     if (tid < nb) {
       const uint32_t mine = sh.ckey[tid];
-      int gt = 0, eq = 0, c = 0;
-      const uint4* c4 = reinterpret_cast<const uint4*>(sh.ckey);
-      for (; c + 4 <= nb; c += 4) {
-        const uint4 o = c4[c >> 2];
-        gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
-        eq += (o.x == mine) + (o.y == mine) + (o.z == mine) + (o.w == mine);
-      }
-      for (; c < nb; ++c) {
+      int gt = 0, eq = 0;
+      for (int c = 0; c < nb; ++c) {
         const uint32_t o = sh.ckey[c];
         gt += o > mine;
         eq += o == mine;
@@ -575,50 +578,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
       }
     }
     __syncthreads();
+    tau = sh.tau;
+    need = sh.need;
   } else {
-    // many: radix levels of up to 11 bits over [lo, lo + span], the range
-    // of bin B's keys, until one key is left
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    visit([&](uint32_t kx, int) {
-      kmin = min(kmin, kx);
-      kmax = max(kmax, kx);
-    });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-    }
-    if (lane == 0) { sh.kred[0][wave] = kmin; sh.kred[1][wave] = kmax; }
-    __syncthreads();
-    uint32_t lo = sh.kred[0][0], hi = sh.kred[1][0];
-#pragma unroll
-    for (int w = 1; w < kTopkWaves; ++w) { lo = min(lo, sh.kred[0][w]); hi = max(hi, sh.kred[1][w]); }
+    // radix levels over [lo, lo + span], the keys of bin B, until one key is
+    // left: 8-bit digits over the LDS list (a small crossing per level),
+    // 11-bit digits when every visit re-reads the workspace
+    uint32_t lo, hi;
+    l1_bin_range(static_cast<int>(B), &lo, &hi);
     uint32_t span = hi - lo;
-    while (span > 0) {  // uniform
-      const int shift = max(0, 21 - __clz(static_cast<int>(span)));  // span >> shift < 2048
-      for (int i = tid; i < kHistWords; i += kTopkThreads) sh.hist2[i] = 0;
-      __syncthreads();
-      visit([&](uint32_t kx, int) {
-        const uint32_t dx = kx - lo;
-        if (kx >= lo && dx <= span) atomicAdd(&sh.hist2[hpad(static_cast<int>(dx >> shift))], 1);
-      });
-      __syncthreads();
-      if (wave == 0) wave_crossing<kBins / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
-      __syncthreads();
-      need -= sh.above[1];
-      const uint32_t dg = static_cast<uint32_t>(min(max(sh.bin[1], 0), kBins - 1)) << shift;
-      lo += dg;
-      span = min(span - dg, (1u << shift) - 1u);
-      __syncthreads();  // bin / above are read before the next level writes them
-    }
-    if (tid == 0) {
-      sh.tau = lo;
-      sh.need = need;
-    }
-    __syncthreads();
+    auto levels = [&](auto dig) {
+      constexpr int DIG = decltype(dig)::value, NBIN = 1 << DIG;
+      while (span > 0) {  // uniform
+        const int shift = max(0, 32 - DIG - __clz(static_cast<int>(span)));  // span >> shift < NBIN
+        for (int i = tid; i < hist_words(NBIN); i += kTopkThreads) sh.hist2[i] = 0;
+        __syncthreads();
+        visit([&](uint32_t kx, int) {
+          const uint32_t dx = kx - lo;
+          if (kx >= lo && dx <= span) atomicAdd(&sh.hist2[hpad(static_cast<int>(dx >> shift))], 1);
+        });
+        __syncthreads();
+        if (wave == 0) wave_crossing<NBIN / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
+        __syncthreads();
+        need -= sh.above[1];
+        const uint32_t dg = static_cast<uint32_t>(min(max(sh.bin[1], 0), NBIN - 1)) << shift;
+        lo += dg;
+        span = min(span - dg, (1u << shift) - 1u);
+        // bin / above are rewritten two barriers later, after every read
+      }
+    };
+    if (in_lds) levels(std::integral_constant<int, 8>{});
+    else levels(std::integral_constant<int, 11>{});
+    tau = lo;
   }
-  const uint32_t tau = sh.tau;
-  need = sh.need;
   // `need` copies of tau are taken (lowest positions first)
 
   // 4. what earlier tiles contribute: greater keys and copies of tau
