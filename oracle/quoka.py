@@ -10,6 +10,10 @@ Sources (web pages, cited by title and section):
     Algorithm 1 and the NQ rule), section 2.2 (cosine score S_ij), section 2.3
     (group-aware aggregation listing), section 4.2 question 3 (FlashAttention
     takes QUOKA's output as its KV input, with its causal mask disabled).
+  * Attention co-design knowledge card ("Co-Designing AI Model Attention for
+    Fast, Interactive Long-Context Inference"), methods list: FP8 KV cache,
+    the storage the 8-bit scoring variant reads.  The E4M3 code table follows
+    the OCP 8-bit floating point specification (OFP8), not the pages.
 
 Every input is widened to fp64 (exact for fp32 and bf16) and all arithmetic is
 fp64.  Readings taken where the pages are silent are stated next to the code
@@ -118,6 +122,78 @@ def key_scores(q_group, k, t_past: int):
     k_norm = kp / np.maximum(_norm(kp), EPS)[..., None]
     s = np.matmul(qg, np.swapaxes(k_norm, -1, -2))
     return s, s.max(axis=2)
+
+
+# --------------------------------------------------------------------------
+# Scoring variants.
+#   * Dot-product scoring: the score that section 2.2 of the QUOKA write-up
+#     measures the cosine score against (its Table 9), read as the section 2.3
+#     listing with both L2 normalisations removed: the group queries are the
+#     plain mean of the kept queries over the G heads, and the keys enter
+#     unnormalised.  Query sub-selection (section 2.1) is unchanged.
+#   * 8-bit keys for the scoring pass: the FP8 KV-cache storage that the
+#     attention co-design knowledge card ("Co-Designing AI Model Attention for
+#     Fast, Interactive Long-Context Inference", methods list) names among the
+#     measured prefill and decode kernels, here in the OCP 8-bit
+#     floating-point format E4M3 (sign, 4 exponent bits with bias 7, 3
+#     mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; the code
+#     S.1111.111 is NaN; no infinities; largest finite 448).  A key is stored
+#     as the code nearest to its value, ties to the even code (even mantissa),
+#     magnitudes above 448 saturating to 448; the sign is kept, so -0.0 and
+#     small negative values that round to zero become the code 0x80.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code (uint8), fp64; NaN for 0x7f and 0xff."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where((c >> 7) == 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = np.ldexp(m / 8.0, -6)
+    val = sign * np.where(e > 0, normal, sub)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+_E4M3_MAG = e4m3_decode(np.arange(0x7F))  # codes 0x00 .. 0x7e: magnitudes 0 .. 448, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code (uint8) of each value: ties go to the even code,
+    magnitudes above 448 saturate to 448, the sign bit follows the value's."""
+    x = f64(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    lo = np.searchsorted(_E4M3_MAG, a, side="right") - 1   # largest magnitude <= a
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = a - _E4M3_MAG[lo]
+    d_hi = _E4M3_MAG[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def group_queries_dot(q, qidx, nkv: int) -> np.ndarray:
+    """Dot-product variant of the group queries: the kept queries, unnormalised,
+    averaged over the G heads of the group.  Shape (b, nkv, NQ, d)."""
+    q = f64(q)
+    b, nq, bcp, d = q.shape
+    G = nq // nkv
+    sel = np.take_along_axis(q, np.asarray(qidx)[..., None], axis=2)   # (b, nq, NQ, d)
+    return sel.reshape(b, nkv, G, sel.shape[2], d).mean(axis=2)
+
+
+def key_scores_dot(q_group, k, t_past: int):
+    """Dot-product variant: S[b,j,n,t] = Q_group[b,j,n] . K[b,j,t] for the T past
+    keys, S_agg = max over n.  Returns (s (b,nkv,NQ,T), s_agg (b,nkv,T))."""
+    s = np.matmul(f64(q_group), np.swapaxes(f64(k[:, :, :t_past]), -1, -2))
+    return s, s.max(axis=2)
+
+
+def scoring_keys_e4m3(k) -> np.ndarray:
+    """The keys the 8-bit scoring pass sees: each element stored as E4M3 and
+    read back (fp64)."""
+    return e4m3_decode(e4m3_encode(k))
 
 
 def select_keys(s_agg, bsa: int) -> np.ndarray:
@@ -238,14 +314,26 @@ def dense_attention(q, k, v, t_past: int, scale=None, rows=None, heads=None):
 # --------------------------------------------------------------------------
 def pipeline(q, k, v, t_past: int, nq_keep: int, bsa: int = 0, scale=None,
              round_off=None, top_rounds: int = 0, rows=None, heads=None,
-             with_attention: bool = True) -> dict:
+             with_attention: bool = True, score: str = "cosine",
+             k_e4m3: bool = False) -> dict:
     """Query sub-selection -> key scoring -> top-BSA (or top rounds) ->
-    attention over the selected keys.  Returns every intermediate."""
+    attention over the selected keys.  Returns every intermediate.
+
+    score: "cosine" (section 2.2, the method) or "dot" (its Table 9 baseline);
+    k_e4m3: the scoring pass sees the keys stored as E4M3 (attention still uses
+    the keys as given)."""
     q = f64(q)
     nkv = k.shape[1]
     qidx, sq = select_queries(q, nq_keep)
-    qg = group_queries(q, qidx, nkv)
-    s, s_agg = key_scores(qg, k, t_past)
+    ks = scoring_keys_e4m3(k[:, :, :t_past]) if k_e4m3 else k
+    if score == "cosine":
+        qg = group_queries(q, qidx, nkv)
+        s, s_agg = key_scores(qg, ks, t_past)
+    elif score == "dot":
+        qg = group_queries_dot(q, qidx, nkv)
+        s, s_agg = key_scores_dot(qg, ks, t_past)
+    else:
+        raise ValueError("score is 'cosine' or 'dot'")
     out = {"sq": sq, "qidx": qidx, "q_group": qg, "s": s, "s_agg": s_agg}
     if round_off is not None:
         s_round = round_scores(s_agg, round_off)

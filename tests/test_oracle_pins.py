@@ -432,6 +432,120 @@ def test_rounds_bruteforce_and_limits():
 # ----------------------------------------------------------------------------
 # 7. the pins catch planted mistakes
 # ----------------------------------------------------------------------------
+# ----------------------------------------------------------------------------
+# scoring variants: E4M3 keys and dot-product scores
+# ----------------------------------------------------------------------------
+def _brute_dot_scores(q, k, qidx, t_past, nkv):
+    """S_agg of the dot-product variant by plain loops: per slot n the mean over
+    the group's heads of the raw kept queries, dotted with the raw keys, then
+    the max over slots."""
+    b, nq, d = len(q), len(q[0]), len(q[0][0][0])
+    G = nq // nkv
+    n_keep = len(qidx[0][0])
+    out = []
+    for bi in range(b):
+        rows = []
+        for j in range(nkv):
+            row = []
+            for t in range(t_past):
+                best = -math.inf
+                for n in range(n_keep):
+                    tot = 0.0
+                    for e in range(d):
+                        avg = sum(q[bi][j * G + g][qidx[bi][j * G + g][n]][e] for g in range(G)) / G
+                        tot += avg * k[bi][j][t][e]
+                    best = max(best, tot)
+                row.append(best)
+            rows.append(row)
+        out.append(rows)
+    return np.array(out)
+
+
+def test_e4m3_code_table():
+    # values fixed by the OCP 8-bit floating point specification, E4M3 column
+    assert Q.e4m3_decode(0x7E) == 448.0                 # largest finite, S.1111.110
+    assert Q.e4m3_decode(0x08) == 2.0 ** -6             # smallest normal, S.0001.000
+    assert Q.e4m3_decode(0x07) == 0.875 * 2.0 ** -6     # largest subnormal, S.0000.111
+    assert Q.e4m3_decode(0x01) == 2.0 ** -9             # smallest subnormal
+    assert Q.e4m3_decode(0x38) == 1.0 and Q.e4m3_decode(0xB8) == -1.0
+    assert np.isnan(Q.e4m3_decode(0x7F)) and np.isnan(Q.e4m3_decode(0xFF))
+    z = Q.e4m3_decode(0x80)
+    assert z == 0.0 and np.signbit(z)
+    assert np.all(np.diff(Q.e4m3_decode(np.arange(0x7F))) > 0)
+    # every code against torch's float8_e4m3fn, an independent implementation
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = Q.e4m3_decode(np.arange(256))
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ref[fin], got[fin])
+    assert np.array_equal(np.signbit(ref[fin]), np.signbit(got[fin]))
+
+
+def test_e4m3_encode_rounding():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    assert np.array_equal(Q.e4m3_encode(Q.e4m3_decode(codes)), codes.astype(np.uint8))
+    # midpoints of neighbouring magnitudes go to the even code; points just off
+    # a midpoint go to the nearer code
+    mags = Q.e4m3_decode(np.arange(0x7F))
+    mid = (mags[:-1] + mags[1:]) / 2
+    lo = np.arange(0x7E)
+    even = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(Q.e4m3_encode(mid), even.astype(np.uint8))
+    assert np.array_equal(Q.e4m3_encode(-mid), (even | 0x80).astype(np.uint8))
+    off = (mags[1:] - mags[:-1]) * 1e-3
+    assert np.array_equal(Q.e4m3_encode(mid - off), lo.astype(np.uint8))
+    assert np.array_equal(Q.e4m3_encode(mid + off), (lo + 1).astype(np.uint8))
+    # saturation above 448, signed zero
+    assert Q.e4m3_encode(1e6) == 0x7E and Q.e4m3_encode(-1e6) == 0xFE
+    assert Q.e4m3_encode(464.0) == 0x7E and Q.e4m3_encode(470.0) == 0x7E
+    assert Q.e4m3_encode(-1e-30) == 0x80 and Q.e4m3_encode(0.0) == 0x00
+    # within range, against torch's round-to-nearest-even conversion from fp32
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 4, rng.standard_normal(5000) * 0.01,
+                        rng.uniform(-460, 460, 5000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(Q.e4m3_encode(x), ref)
+
+
+def test_dot_scores_bruteforce_and_links():
+    rng = np.random.default_rng(6)
+    q, k, _ = _rand_case(rng, b=2, nq=6, nkv=2, d=5, t=9, bcp=6)
+    qi, _ = Q.select_queries(q, 3)
+    _, sa = Q.key_scores_dot(Q.group_queries_dot(q, qi, 2), k, 9)
+    assert np.allclose(sa, _brute_dot_scores(q.tolist(), k.tolist(), qi.tolist(), 9, 2), atol=1e-12)
+    # G = 1: the group queries are the kept rows themselves
+    qi1, _ = Q.select_queries(q, 2)
+    g1 = Q.group_queries_dot(q, qi1, 6)
+    assert np.array_equal(g1, np.take_along_axis(q, qi1[..., None], axis=2))
+    # on unit-norm queries and keys the dot variant equals the cosine scores
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    _, sa_cos = Q.key_scores(Q.group_queries(qn, qi, 2), kn, 9)
+    _, sa_dot = Q.key_scores_dot(Q.group_queries_dot(qn, qi, 2), kn, 9)
+    assert np.allclose(sa_cos, sa_dot, atol=1e-14)
+    # scaling the keys by c > 0 scales the dot scores by c, not the cosine ones
+    _, sa2 = Q.key_scores_dot(Q.group_queries_dot(q, qi, 2), 3.0 * k, 9)
+    assert np.allclose(sa2, 3.0 * sa, atol=1e-12)
+    _, c1 = Q.key_scores(Q.group_queries(q, qi, 2), k, 9)
+    _, c3 = Q.key_scores(Q.group_queries(q, qi, 2), 3.0 * k, 9)
+    assert np.allclose(c1, c3, atol=1e-14)
+
+
+def test_pipeline_variants_compose():
+    rng = np.random.default_rng(7)
+    q, k, v = _rand_case(rng, b=1, nq=4, nkv=2, d=6, t=20, bcp=5)
+    out = Q.pipeline(q, k, v, 20, 3, 7, score="dot", with_attention=False)
+    _, sa = Q.key_scores_dot(Q.group_queries_dot(q, out["qidx"], 2), k, 20)
+    assert np.array_equal(out["s_agg"], sa)
+    assert np.array_equal(out["kidx"], Q.select_keys(sa, 7))
+    out8 = Q.pipeline(q, k, v, 20, 3, 7, k_e4m3=True, with_attention=False)
+    k8 = Q.e4m3_decode(Q.e4m3_encode(k[:, :, :20]))
+    _, sa8 = Q.key_scores(Q.group_queries(q, out8["qidx"], 2), k8, 20)
+    assert np.array_equal(out8["s_agg"], sa8)
+    with pytest.raises(ValueError):
+        Q.pipeline(q, k, v, 20, 3, 7, score="raw")
+
+
 def _pins_pass(mod):
     """Run a compact subset of the pins against a (possibly mutated) module."""
     g, env = _load_worked()
@@ -452,6 +566,13 @@ def _pins_pass(mod):
         qi, _ = mod.select_queries(qq, 3)
         _, sa = mod.key_scores(mod.group_queries(qq, qi, 2), kk, 8)
         ok &= np.allclose(sa, _brute_pipeline_scores(qq.tolist(), kk.tolist(), 8, 3, 2), atol=1e-12)
+        _, sd = mod.key_scores_dot(mod.group_queries_dot(qq, qi, 2), kk, 8)
+        ok &= np.allclose(sd, _brute_dot_scores(qq.tolist(), kk.tolist(), qi.tolist(), 8, 2), atol=1e-12)
+        ok &= mod.e4m3_decode(0x7E) == 448.0 and mod.e4m3_decode(0x01) == 2.0 ** -9
+        mags = mod.e4m3_decode(np.arange(0x7F))
+        lo = np.arange(0x7E)
+        ok &= np.array_equal(mod.e4m3_encode((mags[:-1] + mags[1:]) / 2),
+                             np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8))
         return bool(ok)
     except Exception:
         return False
@@ -470,6 +591,13 @@ MUTATIONS = {
     "no causal mask": ("logits[:, n_past:][hidden] = -np.inf", "pass"),
     "scale dropped": ("sc = 1.0 / math.sqrt(d) if scale is None else float(scale)", "sc = 1.0"),
     "v transposed role": ("o[bi, hi] = (p @ vv) / l", "o[bi, hi] = (p @ kk) / l"),
+    "e4m3 bias 8": ("normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))",
+                    "normal = np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int64))"),
+    "e4m3 ties up": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
+    "dot keeps key norm": ("s = np.matmul(f64(q_group), np.swapaxes(f64(k[:, :, :t_past]), -1, -2))",
+                           "s = np.matmul(f64(q_group), np.swapaxes(f64(k[:, :, :t_past]) / _norm(f64(k[:, :, :t_past]))[..., None], -1, -2))"),
+    "dot sums heads": ("return sel.reshape(b, nkv, G, sel.shape[2], d).mean(axis=2)",
+                       "return sel.reshape(b, nkv, G, sel.shape[2], d).sum(axis=2)"),
 }
 
 
