@@ -68,14 +68,16 @@ def _describe(s) -> str:
                                              if s.n_rounds else ""))
 
 
-def algorithmic(spec, n_sel_per_bj):
+def algorithmic(spec, n_sel_per_bj, key_bytes=None):
     """Per-step algorithmic work.  n_sel_per_bj: mean selected past keys per
-    (sequence, KV head)."""
+    (sequence, KV head); key_bytes: bytes per key element the scoring pass reads
+    (default: the dtype's; 1 for E4M3 keys)."""
     esz = 2 if spec.dtype == "bf16" else 4
+    kesz = esz if key_bytes is None else key_bytes
     bnkv = spec.b * spec.nkv
-    # scoring: every past key read once (d*esz) + one fp32 score written, plus the kept
+    # scoring: every past key read once (d*kesz) + one fp32 score written, plus the kept
     # query rows and their positions (the group queries are formed inside the pass)
-    score_bytes = (bnkv * spec.t_past * (spec.d * esz + 4)
+    score_bytes = (bnkv * spec.t_past * (spec.d * kesz + 4)
                    + spec.b * spec.nq * spec.nq_keep * (spec.d * esz + 4))
     score_flops = 2.0 * bnkv * spec.nq_keep * spec.d * spec.t_past
     # attention: 4*d flops per (query row, attended key); causal chunk counts its half
@@ -95,7 +97,7 @@ def pipe_splits(shape) -> int:
     return 2 if qk.qk_workspace_bytes(shape, "sparse_attn") > 0 else 1
 
 
-def cpu_baseline(spec, seed, budget_s: float):
+def cpu_baseline(spec, seed, budget_s: float, score: str = "cosine", k_e4m3: bool = False):
     """The fp64 oracle, as it stands, on this host: the full chunk if it fits
     the time budget, else a row sample of the attention (selection is always
     complete) scaled to one chunk."""
@@ -112,7 +114,8 @@ def cpu_baseline(spec, seed, budget_s: float):
     off = case["round_off"].numpy() if case["round_off"] is not None else None
     t0 = time.perf_counter()
     sel = oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, round_off=off,
-                          top_rounds=spec.top_rounds, with_attention=False)
+                          top_rounds=spec.top_rounds, with_attention=False, score=score,
+                          k_e4m3=k_e4m3)
     t_sel = time.perf_counter() - t0
     # time attention on growing row samples until the budget is used, then scale
     rows_total = spec.bcp
@@ -135,7 +138,7 @@ def cpu_baseline(spec, seed, budget_s: float):
         while total < 0.5 * budget_s:
             t1 = time.perf_counter()
             oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, round_off=off,
-                            top_rounds=spec.top_rounds)
+                            top_rounds=spec.top_rounds, score=score, k_e4m3=k_e4m3)
             total += time.perf_counter() - t1
             reps += 1
         est, measured = total / reps, total
@@ -162,6 +165,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--gathered", action="store_true", help="qk_gather + qk_sparse_attn instead of the fused path")
+    ap.add_argument("--score", default="cosine", choices=["cosine", "dot"],
+                    help="scoring: the method's cosine score or the dot-product baseline")
+    ap.add_argument("--keys", default="dtype", choices=["dtype", "e4m3"],
+                    help="keys the scoring pass reads: the cache dtype or an 8-bit E4M3 copy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
@@ -196,12 +203,24 @@ def main():
     for c in range(copies):
         case = W.make_case(spec, args.seed + 7919 * c, device=dev)
         inputs.append(case)
+    e4m3 = args.keys == "e4m3"
+    variant = e4m3 or args.score != "cosine"
     pipe = qk.Pipeline(shape, device=dev, n_rounds=spec.n_rounds, top_rounds=spec.top_rounds,
-                       fused_gather=not args.gathered)
+                       fused_gather=not args.gathered, score_mode=args.score, k_e4m3=e4m3)
+    if e4m3:
+        # every copy's cache also held as E4M3 (written once, as the rows were
+        # appended); the timed step converts the chunk's own rows, the append
+        for c in inputs:
+            pipe.k8 = torch.empty(c["k"].shape, dtype=torch.uint8, device=dev)
+            pipe.store_keys_e4m3(c["k"])
+            c["k8"] = pipe.k8
     torch.cuda.synchronize()
 
     def step(i):
         c = inputs[i % copies]
+        if e4m3:
+            pipe.k8 = c["k8"]
+            pipe.store_keys_e4m3(c["k"], spec.t_past, spec.bcp)
         pipe.select(c["q"], c["k"], c["round_off"])
         pipe.attend(c["q"], c["k"], c["v"])
 
@@ -221,11 +240,17 @@ def main():
     # (the launches are enqueued ahead, so host gaps between calls do not
     # count).  A stage reads the previous stage's outputs as they stand, which
     # are valid inputs of the same shape.
-    stages = ["qsel", "kvscore", "select", "attention"]
+    stages = (["store_keys"] if e4m3 else []) + ["qsel", "kvscore", "select", "attention"]
 
     def run_stage(name, c):
-        if name == "qsel":
+        if name == "store_keys":
+            qk.qk_keys_to_e4m3(shape, c["k"], spec.t_past, spec.bcp, c["k8"])
+        elif name == "qsel":
             qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
+        elif name == "kvscore" and variant:
+            qk.qk_kvscore_variant(shape, c["q"], pipe.q_idx, c["k8"] if e4m3 else c["k"],
+                                  qk.QK_KEYS_E4M3 if e4m3 else qk.QK_KEYS_DTYPE, args.score,
+                                  pipe.s_agg)
         elif name == "kvscore":
             qk.qk_kvscore_grouped(shape, c["q"], pipe.q_idx, c["k"], pipe.s_agg)
         elif name == "select":
@@ -253,13 +278,17 @@ def main():
         stage_ms[sname] = e0.elapsed_time(e1) / reps
 
     n_sel = float(pipe.sel_len.float().mean()) if rounds else float(shape.n_sel)
-    work = algorithmic(spec, n_sel)
+    work = algorithmic(spec, n_sel, key_bytes=1 if e4m3 else None)
     score_gbs = work["score_bytes"] / (stage_ms["kvscore"] * 1e-3) / 1e9
     attn_tflops = work["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
-    roof_score = {"kernel": "qk_kvscore_grouped (kvscore_bf16_kernel)", "bound": "hbm",
+    score_kernel = ("qk_kvscore_variant (kvscore_bf16_kernel, "
+                    + ("E4M3 keys, " if e4m3 else "") + f"{args.score} score)" if variant
+                    else "qk_kvscore_grouped (kvscore_bf16_kernel)")
+    roof_score = {"kernel": score_kernel, "bound": "hbm",
                   "achieved": round(score_gbs, 1),
                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-                  "traffic": measured_traffic(spec.name, "kvscore"),
+                  # counters were taken on the default path only
+                  "traffic": None if variant else measured_traffic(spec.name, "kvscore"),
                   "algorithmic_bytes": work["score_bytes"],
                   "ms": round(stage_ms["kvscore"], 5)}
     attn_kernels = ("qk_sparse_attn_indexed (attn_bf16_kernel"
@@ -285,7 +314,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{spec.name}: {_describe(spec)}", "input_copies": copies,
-                   "gather": "gathered" if args.gathered else "fused into attention"},
+                   "gather": "gathered" if args.gathered else "fused into attention",
+                   "score": args.score, "scoring_keys": "e4m3" if e4m3 else spec.dtype},
         "roofline": dominant, "roofline_scoring": roof_score, "roofline_attention": roof_attn,
         "scoring_gbps": round(score_gbs, 1), "scoring_frac_of_peak": round(score_gbs / HBM_PEAK_GBS, 4),
         "keys_scored_per_s": spec.b * spec.nkv * spec.t_past / (stage_ms["kvscore"] * 1e-3),
@@ -315,7 +345,7 @@ def main():
         result["chunk_vs_dense_attention"] = round(dms / ms, 3)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, args.seed, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(spec, args.seed, args.cpu_budget, args.score, e4m3)
         result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 2)
     print(json.dumps(result), flush=True)
 

@@ -10,6 +10,10 @@
  *                   max over the kept queries
  *   qk_kvscore_grouped  same, forming the group queries from the kept
  *                   positions inside the scoring pass
+ *   qk_kvscore_variant  the grouped scoring pass with a choice of score
+ *                   (cosine, or the dot-product baseline) and of key storage
+ *                   (the dtype, or 8-bit E4M3 keys)
+ *   qk_keys_to_e4m3 store key rows as E4M3 bytes for the 8-bit scoring pass
  *   qk_topk         per-row top-k indices of fp32 scores (ascending order)
  *   qk_round_select round-granular variant: round score = max over the round,
  *                   keep the latest round plus the top rounds
@@ -148,6 +152,46 @@ qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k,
  * f32 additionally needs NQ*(d+G)*4 <= 65536 bytes (else QK_ERR_UNSUPPORTED). */
 qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_idx,
                              const void* k, float* s_agg, qk_stream_t stream);
+
+/* Scoring variants of qk_kvscore_variant. */
+typedef enum {
+  QK_SCORE_COSINE = 0, /* the method's score: as qk_kvscore_grouped                  */
+  QK_SCORE_DOT = 1     /* dot-product baseline (QUOKA write-up, section 2.2, its
+                          Table 9 comparison): the listing without its two L2
+                          normalisations,
+                          s_agg[b,j,t] = max over n of
+                            (mean over g < G of q[b,jG+g,q_idx[b,jG+g,n]]) . k[b,j,t] */
+} qk_score_mode;
+typedef enum {
+  QK_KEYS_DTYPE = 0, /* k has s->dtype, (b,nkv,kv_cap,d)                              */
+  QK_KEYS_E4M3 = 1   /* k is (b,nkv,kv_cap,d) uint8 E4M3 codes (qk_keys_to_e4m3); the
+                        scores use the decoded values; needs s->dtype == QK_BF16
+                        (bf16 queries), else QK_ERR_DTYPE                             */
+} qk_key_format;
+
+/* The grouped scoring pass with a choice of score (`mode`, a qk_score_mode) and
+ * key storage (`key_format`, a qk_key_format).  Cosine scoring of dtype keys
+ * equals qk_kvscore_grouped.  8-bit keys halve the bytes the pass streams (the
+ * attention co-design knowledge card, "Co-Designing AI Model Attention for
+ * Fast, Interactive Long-Context Inference", lists FP8 KV caches among its
+ * measured kernels); each code is decoded exactly to bf16 and multiplied on the
+ * matrix cores as in the bf16 path.  Arguments and limits as
+ * qk_kvscore_grouped; an unknown mode or format returns QK_ERR_UNSUPPORTED. */
+qk_status qk_kvscore_variant(const qk_shape* s, const void* q, const int32_t* q_idx,
+                             const void* k, int32_t key_format, int32_t mode, float* s_agg,
+                             qk_stream_t stream);
+
+/* Store rows [row0, row0 + nrows) of every (b, KV head) block of k
+ * ((b,nkv,kv_cap,d), s->dtype) as OCP E4M3 codes at the same element positions
+ * of k8 ((b,nkv,kv_cap,d) uint8, caller-owned): the code nearest to each value,
+ * ties to the even code, magnitudes above 448 (the largest finite code)
+ * saturating to 448, the sign bit kept (OCP 8-bit floating point
+ * specification, E4M3).  Meant to be called on the rows a chunk appends.
+ * Errors: QK_ERR_SHAPE if row0 < 0, nrows < 0 or row0 + nrows > kv_cap;
+ * QK_ERR_ALIGN unless k and k8 are 16-byte aligned.  nrows == 0 launches
+ * nothing.  Inputs must be finite. */
+qk_status qk_keys_to_e4m3(const qk_shape* s, const void* k, int32_t row0, int32_t nrows,
+                          uint8_t* k8, qk_stream_t stream);
 
 /* Per-row top-k of fp32 scores (QUOKA write-up, section 2.3: top-BSA keys per
  * KV head).  scores: (rows, n), row stride ld_scores >= n.  idx: (rows, k)

@@ -25,9 +25,12 @@ LIB_PATH = os.path.join(_HERE, "libqk.so")
 QK_F32, QK_BF16 = 0, 1
 OPS = {"qsel": 0, "kvscore": 1, "topk": 2, "round_select": 3, "gather": 4,
        "sparse_attn": 5, "dense_attn": 6}
+QK_SCORE_COSINE, QK_SCORE_DOT = 0, 1    # qk_score_mode
+QK_KEYS_DTYPE, QK_KEYS_E4M3 = 0, 1      # qk_key_format
+SCORE_MODES = {"cosine": QK_SCORE_COSINE, "dot": QK_SCORE_DOT}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
-            "qk_kvscore", "qk_kvscore_grouped", "qk_topk", "qk_round_select", "qk_gather",
-            "qk_sparse_attn",
+            "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
+            "qk_topk", "qk_round_select", "qk_gather", "qk_sparse_attn",
             "qk_sparse_attn_indexed", "qk_dense_attn"]
 
 
@@ -96,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_qsel": ([F, P, P, P, P, P], I),
         "qk_kvscore": ([F, P, P, P, P], I),
         "qk_kvscore_grouped": ([F, P, P, P, P, P], I),
+        "qk_kvscore_variant": ([F, P, P, P, I, I, P, P], I),
+        "qk_keys_to_e4m3": ([F, P, I, I, P, P], I),
         "qk_topk": ([I, I, I, P, I, P, I, P, SZ, P], I),
         "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P], I),
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
@@ -167,6 +172,22 @@ def qk_kvscore_grouped(shape, q, q_idx, k, s_agg, stream=None):
         _sh(shape), _ptr(q), _ptr(q_idx), _ptr(k), _ptr(s_agg), _stream(stream)))
 
 
+def qk_kvscore_variant(shape, q, q_idx, k, key_format, mode, s_agg, stream=None):
+    """Grouped scoring with a score mode (QK_SCORE_COSINE / QK_SCORE_DOT, or
+    "cosine" / "dot") and key storage (QK_KEYS_DTYPE / QK_KEYS_E4M3)."""
+    mode = SCORE_MODES[mode] if isinstance(mode, str) else int(mode)
+    _check("qk_kvscore_variant", load_library().qk_kvscore_variant(
+        _sh(shape), _ptr(q), _ptr(q_idx), _ptr(k), int(key_format), mode, _ptr(s_agg),
+        _stream(stream)))
+
+
+def qk_keys_to_e4m3(shape, k, row0, nrows, k8, stream=None):
+    """Rows [row0, row0 + nrows) of every (b, KV head) block of k as E4M3 codes
+    at the same positions of the uint8 tensor k8 (same shape as k)."""
+    _check("qk_keys_to_e4m3", load_library().qk_keys_to_e4m3(
+        _sh(shape), _ptr(k), int(row0), int(nrows), _ptr(k8), _stream(stream)))
+
+
 def topk_workspace_bytes(rows: int, n: int) -> int:
     """qk_workspace_bytes(QK_OP_TOPK) for `rows` rows of `n` scores."""
     return qk_workspace_bytes(Shape(rows, 1, 1, 64, 1, n, n + 1, 1, 1), "topk")
@@ -236,12 +257,22 @@ class Pipeline:
     ``fused_group``: the scoring pass forms the group queries itself
     (qk_kvscore_grouped); otherwise qk_qsel writes them to ``q_group`` and
     qk_kvscore reads them.
+
+    ``score_mode``: "cosine" (the method) or "dot" (the dot-product baseline).
+    ``k_e4m3``: the scoring pass reads 8-bit E4M3 keys from ``k8``, which the
+    caller fills with ``store_keys_e4m3`` as rows are appended to the cache
+    (attention still reads the bf16 keys).  Both variants need ``fused_group``.
     """
 
     def __init__(self, shape: Shape, device="cuda", n_rounds: int = 0, top_rounds: int = 0,
                  keep_latest: bool = True, fused_gather: bool = True, with_lse: bool = True,
-                 fused_group: bool = True):
+                 fused_group: bool = True, score_mode: str = "cosine", k_e4m3: bool = False):
         s = self.shape = shape
+        if score_mode not in SCORE_MODES:
+            raise ValueError("score_mode is 'cosine' or 'dot'")
+        if (k_e4m3 or score_mode != "cosine") and not fused_group:
+            raise ValueError("the scoring variants form their group queries (fused_group=True)")
+        self.score_mode, self.k_e4m3 = score_mode, k_e4m3
         self.device = torch.device(device)
         self.n_rounds, self.top_rounds, self.keep_latest = n_rounds, top_rounds, keep_latest
         self.fused_gather, self.fused_group = fused_gather, fused_group
@@ -270,12 +301,24 @@ class Pipeline:
         self.topk_ws_bytes = 0 if n_rounds else topk_workspace_bytes(s.b * s.nkv, s.t_past)
         self.topk_ws = (torch.empty(self.topk_ws_bytes, dtype=torch.uint8, device=dev)
                         if self.topk_ws_bytes else None)
+        self.k8 = (torch.empty((s.b, s.nkv, s.kv_cap, s.d), dtype=torch.uint8, device=dev)
+                   if k_e4m3 else None)
+
+    def store_keys_e4m3(self, k, row0: int = 0, nrows: Optional[int] = None):
+        """Convert key rows [row0, row0 + nrows) (default: to the end of the
+        cache) into the 8-bit copy read by the scoring pass."""
+        nrows = self.shape.kv_cap - row0 if nrows is None else nrows
+        qk_keys_to_e4m3(self.shape, k, row0, nrows, self.k8)
 
     def score(self, q, k):
         """Query sub-selection and key scoring: q_idx, sq and s_agg."""
         s = self.shape
         qk_qsel(s, q, self.q_idx, self.sq, self.q_group)
-        if self.fused_group:
+        if self.k_e4m3 or self.score_mode != "cosine":
+            qk_kvscore_variant(s, q, self.q_idx, self.k8 if self.k_e4m3 else k,
+                               QK_KEYS_E4M3 if self.k_e4m3 else QK_KEYS_DTYPE, self.score_mode,
+                               self.s_agg)
+        elif self.fused_group:
             qk_kvscore_grouped(s, q, self.q_idx, k, self.s_agg)
         else:
             qk_kvscore(s, self.q_group, k, self.s_agg)

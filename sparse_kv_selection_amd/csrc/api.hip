@@ -58,10 +58,12 @@ qk_status check_ws(const qk_shape* s, int32_t op, const void* ws, size_t ws_byte
 }
 
 qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
-                         const int32_t* q_idx, const void* k, float* s_agg, qk_stream_t stream) {
+                         const int32_t* q_idx, const void* k, float* s_agg, qk_stream_t stream,
+                         bool k_e4m3 = false, bool dot = false) {
   qk_status st = check_shape(s);
   if (st != QK_OK) return st;
   if (!k || !s_agg) return QK_ERR_NULL;
+  if (k_e4m3 && !is_bf16(s)) return QK_ERR_DTYPE;
   if (s->nq_keep < 1 || s->nq_keep > s->bcp) return QK_ERR_SHAPE;
   if (is_bf16(s) ? (s->nq_keep > (s->d == 256 ? 32 : 64)) : (s->nq_keep * s->d > 16384))
     return QK_ERR_UNSUPPORTED;
@@ -86,6 +88,8 @@ qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
   c.t_past = s->t_past;
   c.kv_cap = s->kv_cap;
   c.nq_keep = s->nq_keep;
+  c.k_e4m3 = k_e4m3;
+  c.dot = dot;
   return hip_status(qk::launch_kvscore(c, hs(stream)));
 }
 
@@ -142,6 +146,29 @@ qk_status qk_kvscore_grouped(const qk_shape* s, const void* q, const int32_t* q_
                              const void* k, float* s_agg, qk_stream_t stream) {
   if (!q || !q_idx) return QK_ERR_NULL;
   return kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream);
+}
+
+qk_status qk_kvscore_variant(const qk_shape* s, const void* q, const int32_t* q_idx,
+                             const void* k, int32_t key_format, int32_t mode, float* s_agg,
+                             qk_stream_t stream) {
+  if (!q || !q_idx) return QK_ERR_NULL;
+  if ((key_format != QK_KEYS_DTYPE && key_format != QK_KEYS_E4M3) ||
+      (mode != QK_SCORE_COSINE && mode != QK_SCORE_DOT))
+    return QK_ERR_UNSUPPORTED;
+  return kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, key_format == QK_KEYS_E4M3,
+                        mode == QK_SCORE_DOT);
+}
+
+qk_status qk_keys_to_e4m3(const qk_shape* s, const void* k, int32_t row0, int32_t nrows,
+                          uint8_t* k8, qk_stream_t stream) {
+  qk_status st = check_shape(s);
+  if (st != QK_OK) return st;
+  if (!k || !k8) return QK_ERR_NULL;
+  if (row0 < 0 || nrows < 0 || static_cast<int64_t>(row0) + nrows > s->kv_cap) return QK_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(k8)) return QK_ERR_ALIGN;
+  if (nrows == 0) return QK_OK;
+  return hip_status(qk::launch_keys_e4m3(is_bf16(s), k, k8, s->b * s->nkv, s->kv_cap, s->d, row0,
+                                         nrows, hs(stream)));
 }
 
 qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32_t ld_scores,

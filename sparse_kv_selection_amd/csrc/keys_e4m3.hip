@@ -1,0 +1,97 @@
+// Key storage for the 8-bit scoring pass: K rows as OCP E4M3 bytes.
+//
+// The attention co-design knowledge card ("Co-Designing AI Model Attention for
+// Fast, Interactive Long-Context Inference", methods list) names FP8 KV
+// caches among the measured prefill and decode kernels.  Here only the scoring
+// pass reads 8-bit keys: it is bound by the bytes of K it streams, and E4M3
+// halves them.  Attention keeps the bf16 rows.
+//
+// Encoding (OCP 8-bit floating point, E4M3): sign, 4 exponent bits (bias 7),
+// 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6.  Each value
+// takes the nearest code, ties to the even code; magnitudes above 448 (the
+// largest finite code) saturate to 448; the sign bit is copied, so values that
+// round to zero keep it.  Callers convert the rows a chunk appends, once.
+#include "qk_device.h"
+#include "qk_internal.h"
+
+namespace qk {
+namespace {
+
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    // below the smallest normal the codes are the multiples of 2^-9: adding
+    // 2^14 (whose fp32 spacing is 2^-9) rounds to the nearest one, ties to
+    // even; 2^-6 itself comes out as 8, the smallest normal code
+    const float r = __fsub_rn(__fadd_rn(a, 0x1p14f), 0x1p14f);
+    code = static_cast<uint32_t>(r * 512.0f);
+  } else {
+    // keep 3 of the 23 mantissa bits, rounding to nearest even (a carry moves
+    // into the exponent), then rebias the exponent from 127 to 7
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// One thread per 16 consecutive elements of a row (d is a multiple of 16).
+template <typename T>
+__global__ __launch_bounds__(256) void keys_e4m3_kernel(const T* __restrict__ k,
+                                                        uint8_t* __restrict__ k8, int bnkv,
+                                                        int kv_cap, int d, int row0, int nrows) {
+  const int per_row = d / 16;
+  const long long total = static_cast<long long>(bnkv) * nrows * per_row;
+  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int c = static_cast<int>(i % per_row);
+  const long long rr = i / per_row;
+  const int r = static_cast<int>(rr % nrows);
+  const long long bj = rr / nrows;
+  const size_t off = (static_cast<size_t>(bj) * kv_cap + row0 + r) * d + 16 * c;
+  float x[16];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 w = ld16(k + off + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * h + 2 * e] = bf16lo(w[e]);
+        x[8 * h + 2 * e + 1] = bf16hi(w[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(k + off + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * h + e] = w[e];
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    out[w] = e4m3_code(x[4 * w]) | (e4m3_code(x[4 * w + 1]) << 8) | (e4m3_code(x[4 * w + 2]) << 16) |
+             (e4m3_code(x[4 * w + 3]) << 24);
+  st16(k8 + off, out);
+}
+
+}  // namespace
+
+hipError_t launch_keys_e4m3(bool bf16, const void* k, uint8_t* k8, int bnkv, int kv_cap, int d,
+                            int row0, int nrows, hipStream_t st) {
+  const long long total = static_cast<long long>(bnkv) * nrows * (d / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(keys_e4m3_kernel<uint16_t>, grid, block, 0, st,
+                       static_cast<const uint16_t*>(k), k8, bnkv, kv_cap, d, row0, nrows);
+  else
+    hipLaunchKernelGGL(keys_e4m3_kernel<float>, grid, block, 0, st, static_cast<const float*>(k),
+                       k8, bnkv, kv_cap, d, row0, nrows);
+  return hipGetLastError();
+}
+
+}  // namespace qk

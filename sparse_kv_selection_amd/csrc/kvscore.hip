@@ -39,7 +39,7 @@ struct ScoreArgs {
   const float* q_group;    // (b, nkv, nq_keep, d) fp32, or nullptr: formed from q / q_idx
   const uint16_t* q;       // (b, nq, bcp, d) the chunk's queries
   const int32_t* q_idx;    // (b, nq, nq_keep) kept positions
-  const uint16_t* k;
+  const void* k;           // (b, nkv, kv_cap, d) bf16, or E4M3 bytes
   float* s_agg;
   int nkv, group, bcp, t_past, kv_cap, nq_keep;
   int blocks_per_bj, wgs_per_bj;
@@ -74,8 +74,13 @@ struct GroupBuild {
         pos[u][gg] = min(max(qi[g * a.nq_keep + n], 0), a.bcp - 1);
       }
     }
+    // every index load goes out before the first one is used (the scheduler
+    // would otherwise sink each load down to its use and wait on it there)
+    __builtin_amdgcn_sched_barrier(0);
   }
 
+  // DOT: the kept rows enter unnormalised (dot-product scoring variant)
+  template <bool DOT>
   __device__ __forceinline__ void build(const ScoreArgs& a, int bj, uint16_t* s_hi,
                                         uint16_t* s_lo) {
     const int b = bj / a.nkv, j = bj - b * a.nkv;
@@ -96,6 +101,8 @@ struct GroupBuild {
           const int g = min(g0 + gg, a.group - 1);
           x[u][gg] = ld16(qb + (static_cast<size_t>(g) * a.bcp + pos[u][gg]) * D + 8 * c);
         }
+      // all row loads in flight together (see load_pos)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -103,12 +110,15 @@ struct GroupBuild {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) { v[2 * e] = bf16lo(x[u][gg][e]); v[2 * e + 1] = bf16hi(x[u][gg][e]); }
-          float n2 = 0.f;
+          float inv = g0 + gg < a.group ? 1.0f : 0.f;
+          if constexpr (!DOT) {
+            float n2 = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) n2 += v[e] * v[e];
+            for (int e = 0; e < 8; ++e) n2 += v[e] * v[e];
 #pragma unroll
-          for (int o = CH / 2; o > 0; o >>= 1) n2 += __shfl_xor(n2, o);
-          const float inv = g0 + gg < a.group ? 1.0f / fmaxf(sqrtf(n2), kEps) : 0.f;
+            for (int o = CH / 2; o > 0; o >>= 1) n2 += __shfl_xor(n2, o);
+            inv *= 1.0f / fmaxf(sqrtf(n2), kEps);
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[u][e] += v[e] * inv;
         }
@@ -133,9 +143,35 @@ struct GroupBuild {
   }
 };
 
-template <int D, int NQB, int STAGES, bool GROUPED>
-__global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(ScoreArgs a) {
+// Two E4M3 codes (bytes 2 SEL, 2 SEL + 1 of w) as a bf16 pair.  The hardware
+// decode to fp32 is exact, and so is keeping the upper half of the fp32
+// values: an E4M3 value has 3 mantissa bits.
+template <bool SEL>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), SEL);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// FP8: keys are E4M3 bytes; lane (c, h) loads key c's bytes [32j + 16h, +16)
+// per load j and decodes them into the operands of steps 2j and 2j + 1, so
+// step s of lane half h covers d-slots qofs(s, h) .. + 8 (the group queries
+// are read in the same order; a dot product does not depend on the order of
+// d).  DOT: no key norm (dot-product scoring variant).
+template <bool FP8>
+__device__ __forceinline__ int qofs(int s, int half) {
+  return FP8 ? 32 * (s >> 1) + 16 * half + 8 * (s & 1) : 16 * s + 8 * half;
+}
+
+// Waves per SIMD the launch grid counts on (kResident below): two, except for
+// d = 256 and two query blocks, whose registers allow one.
+template <int D, int NQB>
+constexpr int score_waves_per_simd() { return (D == 256 || NQB > 1) ? 1 : 2; }
+
+template <int D, int NQB, int STAGES, bool GROUPED, bool FP8, bool DOT>
+__global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>())) void kvscore_bf16_kernel(ScoreArgs a) {
   constexpr int NS = D / 16;  // k-steps per key
+  constexpr int NL = FP8 ? D / 32 : NS;  // 16-byte loads per key
+  static_assert(GROUPED || (!FP8 && !DOT), "variants form their group queries");
   using GBuild = GroupBuild<D, NQB>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -150,29 +186,33 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(Score
   const int nblk = wi < a.blocks_per_bj ? (a.blocks_per_bj - wi + waves_per_bj - 1) / waves_per_bj : 0;
   auto block_of = [&](int m) { return wi + m * waves_per_bj; };
 
-  const uint16_t* kb = a.k + static_cast<size_t>(bj) * a.kv_cap * D + 8 * half;
+  // this lane's first byte of key row 0 of the (b, KV head)
+  const char* kb = static_cast<const char*>(a.k) +
+                   (static_cast<size_t>(bj) * a.kv_cap * D + (FP8 ? 16 : 8) * half) * (FP8 ? 1 : 2);
   float* out = a.s_agg + static_cast<size_t>(bj) * a.t_past;
 
   GBuild gb;
   if constexpr (GROUPED) gb.load_pos(a, bj, 0);  // kept positions first: a dependent trip
 
-  u32x4 buf[STAGES][NS];
+  u32x4 buf[STAGES][NL];
   auto load_block = [&](int blk, u32x4* dst) {
     const int row = min(blk * kBlock + col, a.kv_cap - 1);
-    const uint16_t* src = kb + static_cast<size_t>(row) * D;
+    const char* src = kb + static_cast<size_t>(row) * D * (FP8 ? 1 : 2);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) dst[s] = ld16(src + 16 * s);
+    for (int s = 0; s < NL; ++s) dst[s] = ld16(src + 32 * s);
   };
-  // first blocks in flight before the query fragments are built
+  // First blocks in flight before the query fragments are built.  The loads
+  // are unconditional (a wave with fewer blocks re-reads its first one, or a
+  // clamped row): behind a branch, the wait before the kept positions' first
+  // use would have to assume that no key load is in flight and wait for all.
 #pragma unroll
-  for (int i = 0; i < STAGES - 1; ++i)
-    if (i < nblk) load_block(block_of(i), buf[i]);
+  for (int i = 0; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
 
   bf16x8 qhi[NQB][NS], qlo[NQB][NS];
   if constexpr (GROUPED) {
     __shared__ __align__(16) uint16_t s_hi[GBuild::ROWS * GBuild::LD];
     __shared__ __align__(16) uint16_t s_lo[GBuild::ROWS * GBuild::LD];
-    gb.build(a, bj, s_hi, s_lo);
+    gb.template build<DOT>(a, bj, s_hi, s_lo);
     __syncthreads();
     if (nblk == 0) return;
 #pragma unroll
@@ -181,7 +221,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(Score
       if (row >= a.nq_keep) row = 0;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = row * GBuild::LD + 16 * s + 8 * half;
+        const int off = row * GBuild::LD + qofs<FP8>(s, half);
         qhi[mb][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_hi + off));
         qlo[mb][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_lo + off));
       }
@@ -219,19 +259,33 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(Score
     float n2 = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 kf = as_bf16x8(w[s]);
+      bf16x8 kf;
+      if constexpr (FP8) {
+        const u32x4& x = w[s >> 1];
+        const uint32_t w0 = (s & 1) ? x[2] : x[0], w1 = (s & 1) ? x[3] : x[1];
+        u32x4 y;
+        y[0] = e4m3x2_to_bf16x2<false>(w0);
+        y[1] = e4m3x2_to_bf16x2<true>(w0);
+        y[2] = e4m3x2_to_bf16x2<false>(w1);
+        y[3] = e4m3x2_to_bf16x2<true>(w1);
+        kf = as_bf16x8(y);
+      } else {
+        kf = as_bf16x8(w[s]);
+      }
       // |k|^2: one packed bf16 dot product per pair (the products are exact in
       // fp32, accumulation in fp32).  The pairs are taken from the bf16x8
       // operand by shuffles: a bit cast of a single 32-bit vector element was
       // observed to read the wrong register at -O3.
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 0, 1),
-                                           __builtin_shufflevector(kf, kf, 0, 1), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 2, 3),
-                                           __builtin_shufflevector(kf, kf, 2, 3), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 4, 5),
-                                           __builtin_shufflevector(kf, kf, 4, 5), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 6, 7),
-                                           __builtin_shufflevector(kf, kf, 6, 7), n2, false);
+      if constexpr (!DOT) {
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 0, 1),
+                                             __builtin_shufflevector(kf, kf, 0, 1), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 2, 3),
+                                             __builtin_shufflevector(kf, kf, 2, 3), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 4, 5),
+                                             __builtin_shufflevector(kf, kf, 4, 5), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kf, kf, 6, 7),
+                                             __builtin_shufflevector(kf, kf, 6, 7), n2, false);
+      }
 #pragma unroll
       for (int mb = 0; mb < NQB; ++mb) {
         acc[mb] = mfma32(qhi[mb][s], kf, acc[mb]);
@@ -244,10 +298,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void kvscore_bf16_kernel(Score
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[mb][r]);
     m = fmaxf(m, __shfl_xor(m, 32));
-    n2 += __shfl_xor(n2, 32);
     const int key = blk * kBlock + col;
-    // m / max(|k|, eps) as m * rsqrt(max(|k|^2, eps^2))
-    if (half == 0 && key < a.t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+    if constexpr (DOT) {
+      if (half == 0 && key < a.t_past) out[key] = m;
+    } else {
+      n2 += __shfl_xor(n2, 32);
+      // m / max(|k|, eps) as m * rsqrt(max(|k|^2, eps^2))
+      if (half == 0 && key < a.t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+    }
   };
 
   // unrolled ring: this wave's m-th block lives in buf[m % STAGES]
@@ -285,7 +343,7 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(ScoreCall c) {
       const float* r = row(e / G, e % G);
       float n2 = 0.f;
       for (int x = 0; x < d; ++x) n2 += r[x] * r[x];
-      inv[e] = 1.0f / fmaxf(sqrtf(n2), kEps);
+      inv[e] = c.dot ? 1.0f : 1.0f / fmaxf(sqrtf(n2), kEps);
     }
     __syncthreads();
     const float inv_g = 1.0f / static_cast<float>(G);
@@ -308,16 +366,22 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(ScoreCall c) {
     for (int e = 0; e < d; ++e) dot += sq[n * d + e] * kr[e];
     m = fmaxf(m, dot);
   }
-  c.s_agg[static_cast<size_t>(bj) * c.t_past + t] = m / fmaxf(sqrtf(n2), kEps);
+  c.s_agg[static_cast<size_t>(bj) * c.t_past + t] = c.dot ? m : m / fmaxf(sqrtf(n2), kEps);
 }
 
 template <int D, int NQB, int STAGES>
-void launch_grid(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+void launch_grid(const ScoreArgs& a, bool fp8, bool dot, dim3 grid, hipStream_t st) {
   const dim3 block(64 * kScoreWaves);
   if (a.q_group)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false, false, false>), grid, block, 0, st, a);
+  else if (!fp8 && !dot)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, false>), grid, block, 0, st, a);
+  else if (!fp8)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, true>), grid, block, 0, st, a);
+  else if (!dot)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, false>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, true>), grid, block, 0, st, a);
 }
 
 template <int D, int NQB>
@@ -327,7 +391,7 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   a.q_group = c.q_group;
   a.q = static_cast<const uint16_t*>(c.q);
   a.q_idx = c.q_idx;
-  a.k = static_cast<const uint16_t*>(c.k);
+  a.k = c.k;
   a.s_agg = c.s_agg;
   a.nkv = c.nkv;
   a.group = c.nq / c.nkv;
@@ -338,7 +402,7 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   a.blocks_per_bj = (c.t_past + kBlock - 1) / kBlock;
   // about as many waves as are resident (two per SIMD where the registers
   // allow, else one), each streaming its share of blocks
-  constexpr long long kResident = (D == 256 || NQB > 1) ? 1024 : 2048;
+  constexpr long long kResident = 1024LL * score_waves_per_simd<D, NQB>();
   const long long total = static_cast<long long>(a.blocks_per_bj) * bnkv;
   long long bpw = (total + kResident - 1) / kResident;
   if (bpw < 2) bpw = 2;
@@ -349,8 +413,8 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   // Blocks kept in flight per wave.  A wave with few blocks to score (short
   // rows) does better with a shallower ring (measured at d = 128: 3 for up to
   // 4 blocks per wave, 4 beyond).
-  if (D == 128 && NQB == 1 && bpw <= 4) launch_grid<D, NQB, 3>(a, grid, st);
-  else launch_grid<D, NQB, 4>(a, grid, st);
+  if (D == 128 && NQB == 1 && bpw <= 4) launch_grid<D, NQB, 3>(a, c.k_e4m3, c.dot, grid, st);
+  else launch_grid<D, NQB, 4>(a, c.k_e4m3, c.dot, grid, st);
 }
 
 }  // namespace

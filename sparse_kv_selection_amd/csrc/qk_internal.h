@@ -20,8 +20,15 @@ struct ScoreCall {
   const void* k;
   float* s_agg;
   int b, nq, nkv, d, bcp, t_past, kv_cap, nq_keep;
+  bool k_e4m3 = false;  // k holds E4M3 bytes (bf16 queries, grouped only)
+  bool dot = false;     // dot-product scoring (grouped only)
 };
 hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
+
+// Rows [row0, row0 + nrows) of every (b, KV head) block of k (bf16 or f32) as
+// E4M3 bytes at the same element positions of k8.
+hipError_t launch_keys_e4m3(bool bf16, const void* k, uint8_t* k8, int bnkv, int kv_cap, int d,
+                            int row0, int nrows, hipStream_t st);
 // LDS bytes of the fp32 scoring kernel when it forms the group queries itself.
 size_t kvscore_f32_lds_bytes(int d, int nq_keep, int group);
 

@@ -338,16 +338,17 @@ constexpr int kRankDirect = 64;  // bin B ranked pair by pair up to this size
 
 // Level-1 bin of an order key (2048 bins), monotone in the key so that every
 // bin above the boundary bin is selected whole.  Each sign gets 1024 bins:
-// 128 per binade of |x| over [2^-8, 2^(1022/128 - 8)) (about 0.0039 to 0.98,
-// where cosine scores lie), one bin for the smaller magnitudes next to zero
-// and one for the larger ones (and NaN) at the end.  The top bits of the key
-// alone would spend most bins on exponents that such scores never reach and
-// put a tenth of a row into one bin.
-constexpr int kFineBase = 119 << 7;  // (exponent, top 7 mantissa bits) of 2^-8
+// 64 per binade of |x| over [2^-8, 2^(1022/64 - 8)) (about 0.0039 to 250:
+// cosine scores and dot products of unit-scale vectors), one bin for the
+// smaller magnitudes next to zero and one for the larger ones (and NaN) at the
+// end.  The top bits of the key alone would spend most bins on exponents that
+// such scores never reach and put a tenth of a row into one bin.
+constexpr int kL1Shift = 17;         // key bits below a bin: 23 - 6 mantissa bits
+constexpr int kFineBase = 119 << 6;  // (exponent, top 6 mantissa bits) of 2^-8
 __device__ __forceinline__ int l1_bin(uint32_t key) {
   const bool pos = key >= 0x80000000u;
   const uint32_t mag = pos ? (key & 0x7fffffffu) : (0x7fffffffu - key);  // bits of |x|
-  const int v = static_cast<int>(mag >> 16) - kFineBase;
+  const int v = static_cast<int>(mag >> kL1Shift) - kFineBase;
   const int i = v < 0 ? 0 : min(v + 1, 1023);
   return pos ? 1024 + i : 1023 - i;
 }
@@ -355,8 +356,9 @@ __device__ __forceinline__ int l1_bin(uint32_t key) {
 __device__ __forceinline__ void l1_bin_range(int b, uint32_t* lo, uint32_t* hi) {
   const bool pos = b >= 1024;
   const int i = pos ? b - 1024 : 1023 - b;
-  const uint32_t mlo = i == 0 ? 0u : static_cast<uint32_t>(kFineBase + i - 1) << 16;
-  const uint32_t mhi = i == 1023 ? 0x7fffffffu : (static_cast<uint32_t>(kFineBase + i) << 16) - 1u;
+  const uint32_t mlo = i == 0 ? 0u : static_cast<uint32_t>(kFineBase + i - 1) << kL1Shift;
+  const uint32_t mhi =
+      i == 1023 ? 0x7fffffffu : (static_cast<uint32_t>(kFineBase + i) << kL1Shift) - 1u;
   *lo = pos ? (0x80000000u | mlo) : (0x7fffffffu - mhi);
   *hi = pos ? (0x80000000u | mhi) : (0x7fffffffu - mlo);
 }
@@ -582,8 +584,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
     need = sh.need;
   } else {
     // radix levels over [lo, lo + span], the keys of bin B, until one key is
-    // left: 8-bit digits over the LDS list (a small crossing per level),
-    // 11-bit digits when every visit re-reads the workspace
+    // left: 9-bit digits over the LDS list (a small crossing per level; a fine
+    // bin's 2^17 keys take two levels), 11-bit digits when every visit
+    // re-reads the workspace
     uint32_t lo, hi;
     l1_bin_range(static_cast<int>(B), &lo, &hi);
     uint32_t span = hi - lo;
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
         // bin / above are rewritten two barriers later, after every read
       }
     };
-    if (in_lds) levels(std::integral_constant<int, 8>{});
+    if (in_lds) levels(std::integral_constant<int, 9>{});
     else levels(std::integral_constant<int, 11>{});
     tau = lo;
   }

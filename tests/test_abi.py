@@ -25,7 +25,7 @@ OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, HIP = range(8)
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qk_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qk_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_are_exported():
@@ -92,6 +92,31 @@ def test_null_and_alignment():
     assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(), _p(), _p(), None, None) == NULL
     assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(FAKE + 4), _p(), _p(), _p(), None) == ALIGN
     assert lib.qk_kvscore_grouped(ctypes.byref(s), _p(), _p(FAKE + 2), _p(), _p(), None) == ALIGN
+
+
+@nogpu
+def test_scoring_variants_reject():
+    lib = qk.load_library()
+    s = _shape()
+    var = lib.qk_kvscore_variant
+    assert var(ctypes.byref(s), None, _p(), _p(), 0, 0, _p(), None) == NULL
+    assert var(ctypes.byref(s), _p(), None, _p(), 0, 0, _p(), None) == NULL
+    assert var(ctypes.byref(s), _p(), _p(), _p(), 2, 0, _p(), None) == UNSUP    # key format
+    assert var(ctypes.byref(s), _p(), _p(), _p(), 0, 2, _p(), None) == UNSUP    # score mode
+    assert var(ctypes.byref(s), _p(), _p(), _p(FAKE + 8), 1, 0, _p(), None) == ALIGN
+    f32 = _shape(dtype=qk.QK_F32)
+    assert var(ctypes.byref(f32), _p(), _p(), _p(), qk.QK_KEYS_E4M3, 0, _p(), None) == DTYPE
+    assert var(None, _p(), _p(), _p(), 0, 0, _p(), None) == NULL
+    conv = lib.qk_keys_to_e4m3
+    assert conv(ctypes.byref(s), None, 0, 10, _p(), None) == NULL
+    assert conv(ctypes.byref(s), _p(), 0, 10, None, None) == NULL
+    assert conv(ctypes.byref(s), _p(), -1, 10, _p(), None) == SHAPE
+    assert conv(ctypes.byref(s), _p(), 0, -1, _p(), None) == SHAPE
+    assert conv(ctypes.byref(s), _p(), 1000, 65, _p(), None) == SHAPE       # past kv_cap = 1064
+    assert conv(ctypes.byref(s), _p(FAKE + 2), 0, 10, _p(), None) == ALIGN
+    assert conv(ctypes.byref(s), _p(), 0, 10, _p(FAKE + 8), None) == ALIGN
+    assert conv(ctypes.byref(_shape(d=96)), _p(), 0, 10, _p(), None) == UNSUP
+    assert conv(ctypes.byref(s), _p(), 1064, 0, _p(), None) == OK           # nothing to do
 
 
 @nogpu

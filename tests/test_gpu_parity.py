@@ -153,6 +153,145 @@ def test_kvscore_grouped(gpu, name):
     assert err <= 5e-5, f"precision regression: {err}"
 
 
+# --------------------------------------------------------------------------
+# scoring variants: 8-bit E4M3 keys, dot-product scores
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_keys_to_e4m3_bit_exact(gpu, dtype):
+    """Key rows stored as E4M3: every byte equals the oracle's nearest-code
+    encoding (ties to even, saturation above 448, signed zero), across ten
+    binades of magnitudes; rows outside the converted range are untouched."""
+    qk = gpu
+    rng = np.random.default_rng(41)
+    b, nkv, cap, d = 2, 3, 700, 128
+    x = rng.standard_normal((b, nkv, cap, d)) * np.exp(rng.uniform(-12.0, 7.0, (b, nkv, cap, 1)))
+    mags = oracle.e4m3_decode(np.arange(0x7F))
+    mid = (mags[:-1] + mags[1:]) / 2                      # exact ties, 126 of them
+    x[0, 0, 40, :126] = mid
+    x[0, 0, 41, :126] = -mid
+    x[1, 2, 50, :] = 0.0
+    x[1, 2, 51, :] = -0.0
+    x[1, 2, 52, :] = np.linspace(-2000.0, 2000.0, d)      # saturation both ways
+    x[1, 1, 60, :] = np.linspace(-3e-3, 3e-3, d)          # subnormal codes
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.from_numpy(x.astype(np.float32)).to(tdt).to(_dev()).contiguous()
+    s = qk.Shape(b, nkv, nkv, d, 1, cap - 1, cap, 1, 1, 0.0, qk.QK_BF16 if dtype == "bf16" else qk.QK_F32)
+    k8 = torch.full((b, nkv, cap, d), 0x55, dtype=torch.uint8, device=_dev())
+    row0, nrows = 37, 600
+    qk.qk_keys_to_e4m3(s, k, row0, nrows, k8)
+    torch.cuda.synchronize()
+    got = k8.cpu().numpy()
+    want = oracle.e4m3_encode(np64(k)[:, :, row0:row0 + nrows])
+    assert np.array_equal(got[:, :, row0:row0 + nrows], want)
+    assert np.all(got[:, :, :row0] == 0x55) and np.all(got[:, :, row0 + nrows:] == 0x55)
+
+
+def _variant_keys(qk, s, spec, case, g, e4m3):
+    """(device keys, key format, fp64 keys the scores see)."""
+    kn = np64(case["k"])
+    if not e4m3:
+        return g["k"], qk.QK_KEYS_DTYPE, kn
+    k8 = torch.empty(g["k"].shape, dtype=torch.uint8, device=_dev())
+    qk.qk_keys_to_e4m3(s, g["k"], 0, s.kv_cap, k8)
+    return k8, qk.QK_KEYS_E4M3, oracle.scoring_keys_e4m3(kn)
+
+
+def _dot_bound(qg, keys, t_past):
+    """Per key, max over the kept slots of sum_e |q_group| |k|: the scale of the
+    rounding error of a dot-product score."""
+    return np.matmul(np.abs(qg), np.swapaxes(np.abs(keys[:, :, :t_past]), -1, -2)).max(axis=2)
+
+
+VARIANTS = [("cosine", True), ("dot", False), ("dot", True)]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("mode,e4m3", VARIANTS)
+def test_kvscore_variant(gpu, name, mode, e4m3):
+    """Scoring variants fed the oracle's kept positions.  Cosine scores of the
+    decoded 8-bit keys keep the bf16 path's precision (the decode is exact);
+    dot-product scores are bounded relative to sum |q_group| |k| (the group
+    queries enter the matrix cores as bf16 high + low parts, about 2^-16)."""
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    s = _shape(spec, qk)
+    if e4m3 and spec.dtype != "bf16":
+        pytest.skip("8-bit keys are scored with bf16 queries")
+    q_idx = torch.from_numpy(ref["qidx"].astype(np.int32)).to(_dev())
+    kin, fmt, keys = _variant_keys(qk, s, spec, case, g, e4m3)
+    s_agg = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    qk.qk_kvscore_variant(s, g["q"], q_idx, kin, fmt, mode, s_agg)
+    torch.cuda.synchronize()
+    if mode == "cosine":
+        _, want = oracle.key_scores(ref["q_group"], keys, s.t_past)
+        assert max_abs(s_agg, want) <= 5e-5
+    else:
+        qg = oracle.group_queries_dot(np64(case["q"]), ref["qidx"], s.nkv)
+        _, want = oracle.key_scores_dot(qg, keys, s.t_past)
+        rel = np.abs(np64(s_agg) - want) / _dot_bound(qg, keys, s.t_past)
+        assert rel.max() <= 3e-5, rel.max()
+
+
+def test_kvscore_variant_cosine_dtype_is_grouped(gpu):
+    """Cosine scoring of dtype keys through the variant entry point is the
+    grouped scoring pass, bit for bit."""
+    qk = gpu
+    spec, case, ref, g = _case("llama_ragged")
+    s = _shape(spec, qk)
+    q_idx = torch.from_numpy(ref["qidx"].astype(np.int32)).to(_dev())
+    a = torch.empty((s.b, s.nkv, s.t_past), dtype=torch.float32, device=_dev())
+    c = torch.empty_like(a)
+    qk.qk_kvscore_grouped(s, g["q"], q_idx, g["k"], a)
+    qk.qk_kvscore_variant(s, g["q"], q_idx, g["k"], qk.QK_KEYS_DTYPE, qk.QK_SCORE_COSINE, c)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("name", ["llama_ragged", "decode_small", "d64_nq40"])
+@pytest.mark.parametrize("mode,e4m3", VARIANTS)
+def test_pipeline_variants_end_to_end(gpu, name, mode, e4m3):
+    """Whole chunk with a scoring variant against the oracle pipeline run with
+    the same variant: kept queries, scores, key sets (near-boundary swaps
+    only) and the attention output over the GPU's own selection."""
+    qk = gpu
+    spec, case, ref0, g = _case(name)
+    s = _shape(spec, qk)
+    qn, kn, vn = np64(case["q"]), np64(case["k"]), np64(case["v"])
+    ref = oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, score=mode, k_e4m3=e4m3,
+                          with_attention=False)
+    pipe = qk.Pipeline(s, device=_dev(), score_mode=mode, k_e4m3=e4m3)
+    if e4m3:
+        pipe.store_keys_e4m3(g["k"])
+    pipe(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    gi = npi(pipe.q_idx)
+    agree = group_agreement(gi, ref["qidx"], s.group)
+    assert agree.mean() >= 0.5
+    keys = oracle.scoring_keys_e4m3(kn) if e4m3 else kn
+    if mode == "dot":
+        bound = _dot_bound(ref["q_group"], keys, s.t_past)
+    s_agg, kidx, out = np64(pipe.s_agg), npi(pipe.idx), np64(pipe.out)
+    G = s.group
+    for b in range(s.b):
+        for j in range(s.nkv):
+            assert_sorted_unique(kidx[b, j], s.t_past)
+            if not agree[b, j]:
+                continue
+            err = np.abs(s_agg[b, j] - ref["s_agg"][b, j])
+            if mode == "dot":
+                assert (err / bound[b, j]).max() <= 3e-5
+                tol = max(BOUNDARY_TOL, 3e-5 * float(bound[b, j].max()))
+            else:
+                assert err.max() <= SCORE_TOL
+                tol = BOUNDARY_TOL
+            assert_set_within_boundary(kidx[b, j], ref["kidx"][b, j], ref["s_agg"][b, j], s.n_sel,
+                                       tol=tol, what=f"kidx b{b} j{j}")
+    # attention over the GPU's own selection, against the oracle on that same set
+    sets = [[kidx[b, j] for j in range(s.nkv)] for b in range(s.b)]
+    o_ref, _ = oracle.attention(qn, kn, vn, spec.t_past, sets)
+    assert max_abs(out, o_ref) <= ATTN_TOL[spec.dtype]
+
+
 def test_kvscore_grouped_unsorted_positions(gpu):
     """The group means pair slot n of every head whatever the positions are:
     kept positions given in an arbitrary (unsorted, repeated) order score like
