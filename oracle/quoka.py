@@ -348,3 +348,60 @@ def pipeline(q, k, v, t_past: int, nq_keep: int, bsa: int = 0, scale=None,
         o, lse = attention(q, k, v, t_past, key_sets, scale, rows, heads)
         out.update(o=o, lse=lse)
     return out
+
+
+# --------------------------------------------------------------------------
+# Whole prompts and layer stacks.
+#   * A prompt runs in chunks of BCP queries (QUOKA write-up, section 2.1: the
+#     chunk size BCP and its NQ rule); the chunk starting at position t takes
+#     positions [0, t) as its past and attends its own keys causally.  Decode
+#     steps (section 5.1, generation) are chunks of one query with NQ = 1.
+#   * Round Attention press release, section 02: past a watershed layer the
+#     layers attend to the history alike, so the top-K made at that layer
+#     serves every layer above it.  Reading: layers below the watershed attend
+#     densely, the watershed layer selects, the layers above attend over its
+#     key sets with their own queries, keys and values.
+# --------------------------------------------------------------------------
+def prompt_chunks(q, k, v, bcp: int, nq_keep: int, bsa: int, n_decode: int = 0,
+                  score: str = "cosine", k_e4m3: bool = False):
+    """q (b, nq, P + n_decode, d): the prompt's P queries, then n_decode decode
+    queries; k, v (b, nkv, >= P + n_decode, d): keys and values of those
+    positions.  The prompt runs in chunks of bcp (the last one may be shorter,
+    with NQ = min(nq_keep, its length)); each decode step is a chunk of one
+    query with NQ = 1.  Returns (o (b, nq, P + n_decode, d), per-step results
+    of `pipeline` in order)."""
+    q = f64(q)
+    total = q.shape[2]
+    prompt = total - n_decode
+    outs, steps = [], []
+    t = 0
+    while t < total:
+        n = min(bcp, prompt - t) if t < prompt else 1
+        keep = min(nq_keep, n) if t < prompt else 1
+        r = pipeline(q[:, :, t:t + n], k, v, t, keep, bsa, score=score, k_e4m3=k_e4m3)
+        outs.append(r["o"])
+        steps.append(r)
+        t += n
+    return np.concatenate(outs, axis=2), steps
+
+
+def layer_stack(qs, ks, vs, t_past: int, nq_keep: int, bsa: int, watershed: int,
+                score: str = "cosine"):
+    """One chunk through a stack of layers: qs[l] (b, nq, bcp, d) and ks[l],
+    vs[l] (b, nkv, >= t_past + bcp, d) per layer l.  Layers below `watershed`
+    attend densely, layer `watershed` runs the whole selection, the layers above
+    attend over its key sets.  Returns (outputs per layer, the key sets)."""
+    if not 0 <= watershed < len(qs):
+        raise ValueError("the watershed is one of the layers")
+    ref = pipeline(qs[watershed], ks[watershed], vs[watershed], t_past, nq_keep, bsa, score=score)
+    sets = ref["key_sets"]
+    outs = []
+    for layer in range(len(qs)):
+        if layer < watershed:
+            o, _ = dense_attention(qs[layer], ks[layer], vs[layer], t_past)
+        elif layer == watershed:
+            o = ref["o"]
+        else:
+            o, _ = attention(qs[layer], ks[layer], vs[layer], t_past, sets)
+        outs.append(o)
+    return outs, sets

@@ -546,6 +546,78 @@ def test_pipeline_variants_compose():
         Q.pipeline(q, k, v, 20, 3, 7, score="raw")
 
 
+# ----------------------------------------------------------------------------
+# whole prompts and layer stacks
+# ----------------------------------------------------------------------------
+def _causal_sdpa(q, k, v):
+    """Causal attention of every position over the positions up to it, by
+    torch's scaled_dot_product_attention (fp64, GQA heads expanded)."""
+    G = q.shape[1] // k.shape[1]
+    qt = torch.from_numpy(np.asarray(q, np.float64))
+    kt = torch.from_numpy(np.asarray(k, np.float64)).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(np.asarray(v, np.float64)).repeat_interleave(G, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).numpy()
+
+
+@pytest.mark.parametrize("bcp", [3, 7, 16])
+def test_prompt_full_budget_is_causal_attention(bcp):
+    """With a budget covering every past position, the chunked prompt plus its
+    decode steps is plain causal attention over the whole sequence, whatever
+    the chunk size (a ragged last chunk included)."""
+    rng = np.random.default_rng(8)
+    b, nq, nkv, d, total, dec = 2, 4, 2, 8, 23, 3
+    q = rng.standard_normal((b, nq, total, d))
+    k = rng.standard_normal((b, nkv, total, d))
+    v = rng.standard_normal((b, nkv, total, d))
+    o, steps = Q.prompt_chunks(q, k, v, bcp, 2, bsa=total, n_decode=dec)
+    assert np.allclose(o, _causal_sdpa(q, k, v), atol=1e-12)
+    prompt = total - dec
+    starts = [st["qidx"].shape[-1] for st in steps]
+    assert len(steps) == -(-prompt // bcp) + dec and starts[-dec:] == [1] * dec
+
+
+def test_prompt_chunk_is_pipeline_and_first_chunk_has_no_past():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 4, 10, 6)) + 1.5 * rng.standard_normal((1, 4, 1, 6))
+    k = rng.standard_normal((1, 2, 10, 6))
+    v = rng.standard_normal((1, 2, 10, 6))
+    o, steps = Q.prompt_chunks(q, k, v, 4, 2, bsa=3)
+    # chunk 0: no past, attention over the chunk alone (causal)
+    assert steps[0]["kidx"].shape == (1, 2, 0)
+    assert np.allclose(o[:, :, :4], _causal_sdpa(q[:, :, :4], k[:, :, :4], v[:, :, :4]), atol=1e-12)
+    # chunk 2 (positions 8, 9) is the one-chunk pipeline at t_past = 8
+    r = Q.pipeline(q[:, :, 8:10], k, v, 8, 2, 3)
+    assert np.array_equal(o[:, :, 8:10], r["o"])
+    # decode steps are one-query chunks with NQ = 1 at their own position
+    o2, steps2 = Q.prompt_chunks(q, k, v, 4, 2, bsa=3, n_decode=2)
+    assert [st["qidx"].shape[-1] for st in steps2] == [2, 2, 1, 1]
+    for t in (8, 9):
+        assert np.array_equal(o2[:, :, t:t + 1], Q.pipeline(q[:, :, t:t + 1], k, v, t, 1, 3)["o"])
+
+
+def test_layer_stack_reuse():
+    rng = np.random.default_rng(10)
+    L, b, nq, nkv, d, t, bcp = 4, 1, 4, 2, 6, 12, 3
+    qs = [rng.standard_normal((b, nq, bcp, d)) + rng.standard_normal((b, nq, 1, d)) for _ in range(L)]
+    ks = [rng.standard_normal((b, nkv, t + bcp, d)) for _ in range(L)]
+    vs = [rng.standard_normal((b, nkv, t + bcp, d)) for _ in range(L)]
+    outs, sets = Q.layer_stack(qs, ks, vs, t, 2, 5, watershed=1)
+    # below the watershed: dense causal attention of the chunk
+    full = np.concatenate([np.zeros((b, nq, t, d)), qs[0]], axis=2)
+    assert np.allclose(outs[0], _causal_sdpa(full, ks[0], vs[0])[:, :, t:], atol=1e-12)
+    # the watershed layer is the one-chunk pipeline; above it, its key sets
+    r = Q.pipeline(qs[1], ks[1], vs[1], t, 2, 5)
+    assert np.array_equal(outs[1], r["o"])
+    for layer in (2, 3):
+        o, _ = Q.attention(qs[layer], ks[layer], vs[layer], t, r["key_sets"])
+        assert np.array_equal(outs[layer], o)
+    # identical layers: the reused selection reproduces the watershed output
+    outs2, _ = Q.layer_stack([qs[0]] * 3, [ks[0]] * 3, [vs[0]] * 3, t, 2, 5, watershed=0)
+    assert np.array_equal(outs2[1], outs2[0]) and np.array_equal(outs2[2], outs2[0])
+    with pytest.raises(ValueError):
+        Q.layer_stack(qs, ks, vs, t, 2, 5, watershed=L)
+
+
 def _pins_pass(mod):
     """Run a compact subset of the pins against a (possibly mutated) module."""
     g, env = _load_worked()
@@ -569,6 +641,14 @@ def _pins_pass(mod):
         _, sd = mod.key_scores_dot(mod.group_queries_dot(qq, qi, 2), kk, 8)
         ok &= np.allclose(sd, _brute_dot_scores(qq.tolist(), kk.tolist(), qi.tolist(), 8, 2), atol=1e-12)
         ok &= mod.e4m3_decode(0x7E) == 448.0 and mod.e4m3_decode(0x01) == 2.0 ** -9
+        qp = rng.standard_normal((1, 2, 9, 4))
+        kp = rng.standard_normal((1, 1, 9, 4))
+        vp = rng.standard_normal((1, 1, 9, 4))
+        op, _ = mod.prompt_chunks(qp, kp, vp, 4, 2, bsa=9, n_decode=2)
+        ok &= np.allclose(op, _causal_sdpa(qp, kp, vp), atol=1e-12)
+        op2, _ = mod.prompt_chunks(qp, kp, vp, 4, 2, bsa=3, n_decode=2)
+        for t in (7, 8):
+            ok &= np.array_equal(op2[:, :, t:t + 1], mod.pipeline(qp[:, :, t:t + 1], kp, vp, t, 1, 3)["o"])
         mags = mod.e4m3_decode(np.arange(0x7F))
         lo = np.arange(0x7E)
         ok &= np.array_equal(mod.e4m3_encode((mags[:-1] + mags[1:]) / 2),
@@ -596,6 +676,10 @@ MUTATIONS = {
     "e4m3 ties up": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
     "dot keeps key norm": ("s = np.matmul(f64(q_group), np.swapaxes(f64(k[:, :, :t_past]), -1, -2))",
                            "s = np.matmul(f64(q_group), np.swapaxes(f64(k[:, :, :t_past]) / _norm(f64(k[:, :, :t_past]))[..., None], -1, -2))"),
+    "chunk past off by one": ("r = pipeline(q[:, :, t:t + n], k, v, t, keep, bsa, score=score, k_e4m3=k_e4m3)",
+                              "r = pipeline(q[:, :, t:t + n], k, v, max(t - 1, 0), keep, bsa, score=score, k_e4m3=k_e4m3)"),
+    "decode keeps the chunk rule": ("n = min(bcp, prompt - t) if t < prompt else 1",
+                                    "n = min(bcp, total - t)"),
     "dot sums heads": ("return sel.reshape(b, nkv, G, sel.shape[2], d).mean(axis=2)",
                        "return sel.reshape(b, nkv, G, sel.shape[2], d).sum(axis=2)"),
 }
