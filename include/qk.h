@@ -215,11 +215,15 @@ qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores,
  *   idx[b,j,0..sel_len) = every position of the chosen rounds, ascending
  * idx: (b,nkv,ld_idx) int32 with ld_idx >= the largest possible selection
  * (t_past is always enough); sel_len: (b,nkv) int32; s_round: (b,nkv,n_rounds)
- * f32 or NULL.  1 <= top_r, top_r + (keep_latest != 0) <= n_rounds <= 4096. */
+ * f32 or NULL; chosen: (b,nkv,n_rounds) uint8 or NULL, 1 where round r is one
+ * of head (b,j)'s chosen rounds, else 0 (what a caller that keeps rounds off
+ * the GPU needs to know to bring them in).  1 <= top_r, top_r +
+ * (keep_latest != 0) <= n_rounds <= 4096. */
 qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,
                           const int32_t* round_off, int32_t top_r,
                           int32_t keep_latest, int32_t* idx, int32_t ld_idx,
-                          int32_t* sel_len, float* s_round, qk_stream_t stream);
+                          int32_t* sel_len, float* s_round, uint8_t* chosen,
+                          qk_stream_t stream);
 
 /* Gather the selected rows (QUOKA write-up, section 4.2 question 3: the
  * selection is the attention's KV input).

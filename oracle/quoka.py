@@ -386,14 +386,16 @@ def prompt_chunks(q, k, v, bcp: int, nq_keep: int, bsa: int, n_decode: int = 0,
 
 
 def layer_stack(qs, ks, vs, t_past: int, nq_keep: int, bsa: int, watershed: int,
-                score: str = "cosine"):
+                score: str = "cosine", round_off=None, top_rounds: int = 0):
     """One chunk through a stack of layers: qs[l] (b, nq, bcp, d) and ks[l],
     vs[l] (b, nkv, >= t_past + bcp, d) per layer l.  Layers below `watershed`
-    attend densely, layer `watershed` runs the whole selection, the layers above
+    attend densely, layer `watershed` runs the whole selection (top-BSA keys,
+    or with `round_off` the latest round plus the top rounds), the layers above
     attend over its key sets.  Returns (outputs per layer, the key sets)."""
     if not 0 <= watershed < len(qs):
         raise ValueError("the watershed is one of the layers")
-    ref = pipeline(qs[watershed], ks[watershed], vs[watershed], t_past, nq_keep, bsa, score=score)
+    ref = pipeline(qs[watershed], ks[watershed], vs[watershed], t_past, nq_keep, bsa, score=score,
+                   round_off=round_off, top_rounds=top_rounds)
     sets = ref["key_sets"]
     outs = []
     for layer in range(len(qs)):

@@ -102,7 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_kvscore_variant": ([F, P, P, P, I, I, P, P], I),
         "qk_keys_to_e4m3": ([F, P, I, I, P, P], I),
         "qk_topk": ([I, I, I, P, I, P, I, P, SZ, P], I),
-        "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P], I),
+        "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P, P], I),
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
         "qk_sparse_attn": ([F, P, P, P, I, P, P, P, P, P, P, SZ, P], I),
         "qk_sparse_attn_indexed": ([F, P, P, P, P, I, P, P, P, P, SZ, P], I),
@@ -203,10 +203,10 @@ def qk_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws=None, ws_bytes=0, str
 
 
 def qk_round_select(shape, s_agg, n_rounds, round_off, top_r, keep_latest, idx, ld_idx,
-                    sel_len, s_round=None, stream=None):
+                    sel_len, s_round=None, chosen=None, stream=None):
     _check("qk_round_select", load_library().qk_round_select(
         _sh(shape), _ptr(s_agg), n_rounds, _ptr(round_off), top_r, int(keep_latest), _ptr(idx),
-        ld_idx, _ptr(sel_len), _ptr(s_round), _stream(stream)))
+        ld_idx, _ptr(sel_len), _ptr(s_round), _ptr(chosen), _stream(stream)))
 
 
 def qk_gather(shape, k, v, idx, ld_idx, sel_len, k_sel, v_sel, stream=None):
@@ -287,10 +287,12 @@ class Pipeline:
             self.ld_idx = max(s.t_past, 1)
             self.sel_len = torch.empty((s.b, s.nkv), dtype=i32, device=dev)
             self.s_round = torch.empty((s.b, s.nkv, n_rounds), dtype=f32, device=dev)
+            self.chosen = torch.empty((s.b, s.nkv, n_rounds), dtype=torch.uint8, device=dev)
         else:
             self.ld_idx = max(s.n_sel, 1)
             self.sel_len = None
             self.s_round = None
+            self.chosen = None
         self.idx = torch.empty((s.b, s.nkv, self.ld_idx), dtype=i32, device=dev)
         if not fused_gather:
             self.k_sel = torch.empty((s.b, s.nkv, self.ld_idx, s.d), dtype=s.torch_dtype, device=dev)
@@ -328,7 +330,8 @@ class Pipeline:
         self.score(q, k)
         if self.n_rounds:
             qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds,
-                            self.keep_latest, self.idx, self.ld_idx, self.sel_len, self.s_round)
+                            self.keep_latest, self.idx, self.ld_idx, self.sel_len, self.s_round,
+                            self.chosen)
         else:
             qk_topk(s.b * s.nkv, s.t_past, s.bsa, self.s_agg, self.s_agg.shape[-1], self.idx,
                     self.ld_idx, self.topk_ws, self.topk_ws_bytes)

@@ -192,7 +192,7 @@ qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32
 qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,
                           const int32_t* round_off, int32_t top_r, int32_t keep_latest,
                           int32_t* idx, int32_t ld_idx, int32_t* sel_len, float* s_round,
-                          qk_stream_t stream) {
+                          uint8_t* chosen, qk_stream_t stream) {
   qk_status st = check_shape(s);
   if (st != QK_OK) return st;
   if (!s_agg || !round_off || !idx || !sel_len) return QK_ERR_NULL;
@@ -204,7 +204,7 @@ qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_round
     return QK_ERR_ALIGN;
   return hip_status(qk::launch_round_select(s_agg, s->b * s->nkv, s->t_past, n_rounds, round_off,
                                             top_r, keep_latest ? 1 : 0, idx, ld_idx, sel_len,
-                                            s_round, hs(stream)));
+                                            s_round, chosen, hs(stream)));
 }
 
 qk_status qk_gather(const qk_shape* s, const void* k, const void* v, const int32_t* idx,

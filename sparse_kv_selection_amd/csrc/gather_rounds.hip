@@ -81,7 +81,7 @@ __device__ int round_excl_scan(int v, int* wsum, int* total) {
 __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
     const float* __restrict__ s_agg, int t_past, int n_rounds, const int32_t* __restrict__ off,
     int top_r, int keep_latest, int32_t* __restrict__ idx, int ld_idx,
-    int32_t* __restrict__ sel_len, float* __restrict__ s_round_out) {
+    int32_t* __restrict__ sel_len, float* __restrict__ s_round_out, uint8_t* __restrict__ chosen_out) {
   extern __shared__ int sm[];
   int* so = sm;                                           // [n_rounds + 1] clamped offsets
   uint32_t* rkey = reinterpret_cast<uint32_t*>(so + n_rounds + 1);  // [n_rounds] max keys
@@ -138,6 +138,7 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
       chosen = rank < top_r;
     }
     base[r] = chosen ? 1 : -1;
+    if (chosen_out) chosen_out[static_cast<size_t>(bj) * n_rounds + r] = chosen ? 1 : 0;
   }
   __syncthreads();
 
@@ -185,10 +186,11 @@ hipError_t launch_gather(int esz, const void* k, const void* v, const int32_t* i
 
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,
                                const int32_t* off, int top_r, int keep_latest, int32_t* idx,
-                               int ld_idx, int32_t* sel_len, float* s_round, hipStream_t st) {
+                               int ld_idx, int32_t* sel_len, float* s_round, uint8_t* chosen,
+                               hipStream_t st) {
   const size_t shm = sizeof(int) * (3 * static_cast<size_t>(n_rounds) + 1);
   hipLaunchKernelGGL(round_select_kernel, dim3(bnkv), dim3(kRoundThreads), shm, st, s_agg, t_past,
-                     n_rounds, off, top_r, keep_latest, idx, ld_idx, sel_len, s_round);
+                     n_rounds, off, top_r, keep_latest, idx, ld_idx, sel_len, s_round, chosen);
   return hipGetLastError();
 }
 

@@ -108,12 +108,15 @@ class PromptRunner:
 def layer_stack_step(qs: Sequence[torch.Tensor], caches: Sequence[KVCache],
                      k_rows: Sequence[torch.Tensor], v_rows: Sequence[torch.Tensor],
                      nq_keep: int, bsa: int, watershed: int, score_mode: str = "cosine",
-                     scale: float = 0.0):
+                     scale: float = 0.0, round_off: Optional[torch.Tensor] = None,
+                     top_rounds: int = 0):
     """One chunk through a stack of layers with one cache each (all at the
     same length).  Layers below `watershed` attend densely; the watershed
-    layer selects; the layers above attend over its index list with their own
-    queries, keys and values.  Returns (outputs per layer, the Pipeline of the
-    watershed layer, whose `idx` holds the shared selection)."""
+    layer selects (top-BSA keys, or with `round_off` the latest round plus
+    `top_rounds` more; `bsa` then only sizes the attention plan); the layers
+    above attend over its index list with their own queries, keys and values.
+    Returns (outputs per layer, the Pipeline of the watershed layer, whose
+    `idx` / `sel_len` hold the shared selection)."""
     if not 0 <= watershed < len(qs):
         raise ValueError("the watershed is one of the layers")
     if len({c.length for c in caches}) != 1:
@@ -124,10 +127,12 @@ def layer_stack_step(qs: Sequence[torch.Tensor], caches: Sequence[KVCache],
         c.append(kr, vr, shape)
     dev = qs[0].device
     cw = caches[watershed]
-    pipe = Pipeline(shape, device=dev, score_mode=score_mode, k_e4m3=cw.k8 is not None)
+    n_rounds = 0 if round_off is None else round_off.numel() - 1
+    pipe = Pipeline(shape, device=dev, score_mode=score_mode, k_e4m3=cw.k8 is not None,
+                    n_rounds=n_rounds, top_rounds=top_rounds)
     if cw.k8 is not None:
         pipe.k8 = cw.k8
-    pipe.select(qs[watershed], cw.k)
+    pipe.select(qs[watershed], cw.k, round_off)
     dws, dws_bytes = _ws(shape, "dense_attn", dev)
     outs = []
     for layer, (q, c) in enumerate(zip(qs, caches)):
@@ -141,3 +146,133 @@ def layer_stack_step(qs: Sequence[torch.Tensor], caches: Sequence[KVCache],
     for c in caches:
         c.advance(n)
     return outs, pipe
+
+
+class RoundOffloadStack:
+    """A layer stack with round selection at a watershed layer whose upper
+    layers keep their history in pinned host memory, one block per round.
+
+    Round Attention press release, section 02: each round's KV is split at the
+    watershed layer into a lower block (the layers up to it) and an upper block
+    (the layers above), stored per round in host memory and moved to the GPU a
+    whole round at a time, once the watershed layer has chosen its rounds.
+    Here the lower layers' caches stay on the GPU (they attend densely, and
+    the watershed layer scores every round); the upper block of round r for
+    layer l is one pinned host tensor (2, b, nkv, len_r, d).  After selection,
+    every round chosen by some KV head is copied to the GPU once per upper
+    layer, on a copy stream, into one of two position-addressed staging caches
+    that alternate between layers, so the copies for a layer overlap the
+    attention of the layer before it.  The upper layers attend over the
+    watershed's index list exactly as if their caches were resident."""
+
+    def __init__(self, n_layers: int, watershed: int, round_off: Sequence[int], b: int, nkv: int,
+                 d: int, bcp: int, dtype=torch.bfloat16, device="cuda"):
+        if not 0 <= watershed < n_layers - 1:
+            raise ValueError("the watershed has layers above it")
+        dev = torch.device(device)
+        self.L, self.w, self.device = n_layers, watershed, dev
+        self.off = [int(x) for x in round_off]
+        self.R, self.T = len(self.off) - 1, self.off[-1]
+        self.b, self.nkv, self.d, self.bcp, self.dtype = b, nkv, d, bcp, dtype
+        cap = self.T + bcp
+        self.round_off_dev = torch.tensor(self.off, dtype=torch.int32, device=dev)
+        self.lower = [KVCache(b, nkv, cap, d, dtype, dev) for _ in range(watershed + 1)]
+        self.host = [[torch.empty((2, b, nkv, self.off[r + 1] - self.off[r], d), dtype=dtype,
+                                  pin_memory=True) for r in range(self.R)]
+                     for _ in range(n_layers - watershed - 1)]
+        self.stage = [torch.zeros((2, b, nkv, cap, d), dtype=dtype, device=dev) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(device=dev)
+        self.chosen_host = torch.empty((b, nkv, self.R), dtype=torch.uint8, pin_memory=True)
+        self.last_h2d_bytes = 0
+        self.last_rounds: List[int] = []
+
+    def load_history(self, layer: int, k: torch.Tensor, v: torch.Tensor):
+        """Keys and values (b, nkv, >= T, d) of the T past positions of a layer."""
+        T = self.T
+        if layer <= self.w:
+            c = self.lower[layer]
+            c.k[:, :, :T].copy_(k[:, :, :T])
+            c.v[:, :, :T].copy_(v[:, :, :T])
+            c.length = T
+        else:
+            for r, blk in enumerate(self.host[layer - self.w - 1]):
+                blk[0].copy_(k[:, :, self.off[r]:self.off[r + 1]])
+                blk[1].copy_(v[:, :, self.off[r]:self.off[r + 1]])
+
+    def _layer_bytes(self) -> int:
+        esz = torch.empty((), dtype=self.dtype).element_size()
+        return 2 * self.b * self.nkv * (self.T + self.bcp) * self.d * esz
+
+    def device_kv_bytes(self) -> int:
+        """KV bytes this stack holds on the GPU (lower caches and staging)."""
+        return (len(self.lower) + len(self.stage)) * self._layer_bytes()
+
+    def resident_kv_bytes(self) -> int:
+        """KV bytes every layer's cache would take on the GPU."""
+        return self.L * self._layer_bytes()
+
+    def step(self, qs: Sequence[torch.Tensor], k_rows: Sequence[torch.Tensor],
+             v_rows: Sequence[torch.Tensor], nq_keep: int, top_rounds: int, bsa_plan: int):
+        """One chunk of bcp queries at position T through every layer.  The
+        chunk's own key and value rows sit at [T, T + bcp) of the lower caches
+        and of the staging caches; they are not added to the history, so steps
+        may repeat over one loaded history.  Returns (outputs per layer, the
+        watershed's Pipeline)."""
+        w, T, n = self.w, self.T, qs[0].shape[2]
+        if n != self.bcp:
+            raise ValueError("the stack is sized for chunks of bcp queries")
+        compute = torch.cuda.current_stream(self.device)
+        shape = self.lower[0].shape(qs[0].shape[1], n, min(nq_keep, n), bsa_plan)
+        for layer in range(w + 1):
+            self.lower[layer].append(k_rows[layer], v_rows[layer], shape)
+        dws, dws_bytes = _ws(shape, "dense_attn", self.device)
+        outs: List[torch.Tensor] = []
+        for layer in range(w):
+            out = torch.empty_like(qs[layer])
+            c = self.lower[layer]
+            qk_dense_attn(shape, qs[layer], c.k, c.v, out, None, dws, dws_bytes)
+            outs.append(out)
+        cw = self.lower[w]
+        pipe = Pipeline(shape, device=self.device, n_rounds=self.R, top_rounds=top_rounds)
+        pipe.select(qs[w], cw.k, self.round_off_dev)
+        selected = torch.cuda.Event()
+        selected.record(compute)
+        out = torch.empty_like(qs[w])
+        qk_sparse_attn_indexed(shape, qs[w], cw.k, cw.v, pipe.idx, pipe.ld_idx, pipe.sel_len, out,
+                               None, pipe.ws, pipe.ws_bytes)
+        outs.append(out)
+        # the rounds to bring in: those chosen by some KV head (the host waits
+        # for the selection only; the watershed's attention keeps the GPU busy)
+        with torch.cuda.stream(self.copy_stream):
+            self.copy_stream.wait_event(selected)
+            self.chosen_host.copy_(pipe.chosen, non_blocking=True)
+        self.copy_stream.synchronize()
+        need = self.chosen_host.reshape(-1, self.R).amax(dim=0)
+        rounds = [r for r in range(self.R) if int(need[r])]
+        done: List[torch.cuda.Event] = []
+        h2d = 0
+        for i, layer in enumerate(range(w + 1, self.L)):
+            st = self.stage[i % 2]
+            with torch.cuda.stream(self.copy_stream):
+                if i >= 2:
+                    self.copy_stream.wait_event(done[i - 2])  # that staging cache is free again
+                blocks = self.host[i]
+                for r in rounds:  # one host-to-device copy per round
+                    st[:, :, :, self.off[r]:self.off[r + 1]].copy_(blocks[r], non_blocking=True)
+                    h2d += blocks[r].numel() * blocks[r].element_size()
+                st[0, :, :, T:T + n].copy_(k_rows[layer])
+                st[1, :, :, T:T + n].copy_(v_rows[layer])
+                staged = torch.cuda.Event()
+                staged.record(self.copy_stream)
+            for t in (k_rows[layer], v_rows[layer]):
+                t.record_stream(self.copy_stream)
+            compute.wait_event(staged)
+            out = torch.empty_like(qs[layer])
+            qk_sparse_attn_indexed(shape, qs[layer], st[0], st[1], pipe.idx, pipe.ld_idx,
+                                   pipe.sel_len, out, None, pipe.ws, pipe.ws_bytes)
+            outs.append(out)
+            ev = torch.cuda.Event()
+            ev.record(compute)
+            done.append(ev)
+        self.last_h2d_bytes, self.last_rounds = h2d, rounds
+        return outs, pipe

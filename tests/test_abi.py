@@ -157,11 +157,11 @@ def test_round_select_rejects():
     lib = qk.load_library()
     s = _shape()
     f = lib.qk_round_select
-    assert f(ctypes.byref(s), _p(), 0, _p(), 1, 1, _p(), 1000, _p(), None, None) == SHAPE
-    assert f(ctypes.byref(s), _p(), 8, _p(), 8, 1, _p(), 1000, _p(), None, None) == SHAPE
-    assert f(ctypes.byref(s), _p(), 8, _p(), 0, 1, _p(), 1000, _p(), None, None) == SHAPE
-    assert f(ctypes.byref(s), _p(), 8, _p(), 2, 1, _p(), 999, _p(), None, None) == SHAPE
-    assert f(ctypes.byref(s), _p(), 8, None, 2, 1, _p(), 1000, _p(), None, None) == NULL
+    assert f(ctypes.byref(s), _p(), 0, _p(), 1, 1, _p(), 1000, _p(), None, None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 8, 1, _p(), 1000, _p(), None, None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 0, 1, _p(), 1000, _p(), None, None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, _p(), 2, 1, _p(), 999, _p(), None, None, None) == SHAPE
+    assert f(ctypes.byref(s), _p(), 8, None, 2, 1, _p(), 1000, _p(), None, None, None) == NULL
 
 
 @nogpu

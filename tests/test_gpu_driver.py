@@ -126,3 +126,58 @@ def test_layer_stack_watershed_reuse(gpu):
         o_ref, _ = oracle.attention(qn[layer], kn[layer], vn[layer], t_past, sets)
         assert max_abs(outs[layer], o_ref) <= ATTN_TOL["bf16"], layer
     assert all(c.length == t_past + bcp for c in caches)
+
+
+def test_round_offload_matches_resident_stack(gpu):
+    """Upper layers held per round in host memory: every layer's output equals
+    the resident stack's bit for bit; the copies are the rounds some KV head
+    chose, once per upper layer; the watershed's rounds agree with the
+    oracle's (near-tie swaps only) and the upper layers with the oracle's
+    attention over the GPU's key sets; the GPU holds fewer KV bytes."""
+    from sparse_kv_selection_amd import driver
+    L, w, T, bcp, R, top = 5, 1, 3000, 128, 12, 3
+    off = W.round_offsets(T, R, 11)
+    layers = _sequence(T + bcp, 4001, layers=L)
+    stack = driver.RoundOffloadStack(L, w, off, 1, NKV, D_HEAD, bcp, device=_dev())
+    caches = []
+    for layer, (q, k, v) in enumerate(layers):
+        stack.load_history(layer, k, v)
+        c = driver.KVCache(1, NKV, T + bcp, D_HEAD, device=_dev())
+        c.k[:, :, :T].copy_(k[:, :, :T])
+        c.v[:, :, :T].copy_(v[:, :, :T])
+        c.advance(T)
+        caches.append(c)
+    qs = [q[:, :, T:].contiguous() for (q, _, _) in layers]
+    krows = [k[:, :, T:].contiguous() for (_, k, _) in layers]
+    vrows = [v[:, :, T:].contiguous() for (_, _, v) in layers]
+    outs, pipe = stack.step(qs, krows, vrows, 16, top, bsa_plan=T // 4)
+    off_dev = torch.tensor(off, dtype=torch.int32, device=_dev())
+    outs_r, pipe_r = driver.layer_stack_step(qs, caches, krows, vrows, 16, T // 4, w,
+                                             round_off=off_dev, top_rounds=top)
+    torch.cuda.synchronize()
+    for layer in range(L):
+        assert torch.equal(outs[layer], outs_r[layer]), layer
+    assert torch.equal(pipe.sel_len, pipe_r.sel_len)
+    chosen = npi(pipe.chosen)
+    union = [r for r in range(R) if chosen[..., r].any()]
+    assert stack.last_rounds == union
+    lens = np.diff(np.asarray(off))
+    assert stack.last_h2d_bytes == (L - w - 1) * sum(2 * NKV * int(lens[r]) * D_HEAD * 2 for r in union)
+    assert stack.device_kv_bytes() < stack.resident_kv_bytes()
+    # the watershed's rounds against the oracle's (the latest round is always kept)
+    qn = [np64(x) for x in qs]
+    kn = [np64(k) for (_, k, _) in layers]
+    vn = [np64(v) for (_, _, v) in layers]
+    ref = oracle.pipeline(qn[w], kn[w], vn[w], T, 16, 0, round_off=np.asarray(off), top_rounds=top,
+                          with_attention=False)
+    for j in range(NKV):
+        got = np.flatnonzero(chosen[0, j])
+        want = np.asarray(ref["rounds"][0][j])
+        sr = np.asarray(ref["s_round"][0, j], dtype=np.float64).copy()
+        sr[R - 1] = np.inf
+        assert_set_within_boundary(got, want, sr, top + 1, what=f"rounds j{j}")
+    idx, sl = npi(pipe.idx), npi(pipe.sel_len)
+    sets = [[idx[0, j, :sl[0, j]] for j in range(NKV)]]
+    for layer in (w, w + 1, L - 1):
+        o_ref, _ = oracle.attention(qn[layer], kn[layer], vn[layer], T, sets)
+        assert max_abs(outs[layer], o_ref) <= ATTN_TOL["bf16"], layer

@@ -465,14 +465,21 @@ def test_round_select_and_attention(gpu, name):
     idx = torch.full((s.b, s.nkv, s.t_past), -1, dtype=torch.int32, device=dev)
     sel_len = torch.empty((s.b, s.nkv), dtype=torch.int32, device=dev)
     s_round = torch.empty((s.b, s.nkv, spec.n_rounds), dtype=torch.float32, device=dev)
+    chosen_mask = torch.full((s.b, s.nkv, spec.n_rounds), 7, dtype=torch.uint8, device=dev)
     qk.qk_round_select(s, torch.from_numpy(scores32).to(dev), spec.n_rounds, g["round_off"],
-                       spec.top_rounds, True, idx, s.t_past, sel_len, s_round)
+                       spec.top_rounds, True, idx, s.t_past, sel_len, s_round, chosen_mask)
     torch.cuda.synchronize()
     off = case["round_off"].numpy()
     want_sr = oracle.round_scores(scores32.astype(np.float64), off)
     assert np.array_equal(np64(s_round), want_sr)      # max of fp32 values: exact
     chosen = oracle.select_rounds(want_sr, spec.top_rounds)
     sets = oracle.round_key_sets(chosen, off)
+    cm = npi(chosen_mask)
+    for b in range(s.b):
+        for j in range(s.nkv):
+            want_mask = np.zeros(spec.n_rounds, dtype=np.int64)
+            want_mask[np.asarray(chosen[b][j])] = 1
+            assert np.array_equal(cm[b, j], want_mask)
     gi, gl = npi(idx), npi(sel_len)
     for b in range(s.b):
         for j in range(s.nkv):

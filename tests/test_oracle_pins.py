@@ -616,6 +616,19 @@ def test_layer_stack_reuse():
     assert np.array_equal(outs2[1], outs2[0]) and np.array_equal(outs2[2], outs2[0])
     with pytest.raises(ValueError):
         Q.layer_stack(qs, ks, vs, t, 2, 5, watershed=L)
+    # round selection at the watershed: the layers above attend over the
+    # positions of its chosen rounds
+    off = np.array([0, 3, 7, 12])
+    outs_r, sets_r = Q.layer_stack(qs, ks, vs, t, 2, 0, watershed=1, round_off=off, top_rounds=1)
+    rr = Q.pipeline(qs[1], ks[1], vs[1], t, 2, 0, round_off=off, top_rounds=1)
+    for j in range(nkv):
+        assert np.array_equal(sets_r[0][j], rr["key_sets"][0][j])
+        chosen = set(np.asarray(rr["rounds"][0][j]).tolist())
+        assert 2 in chosen and len(chosen) == 2          # the latest round plus one
+        want = np.concatenate([np.arange(off[r], off[r + 1]) for r in sorted(chosen)])
+        assert np.array_equal(sets_r[0][j], want)
+    o3, _ = Q.attention(qs[3], ks[3], vs[3], t, rr["key_sets"])
+    assert np.array_equal(outs_r[3], o3)
 
 
 def _pins_pass(mod):
