@@ -153,6 +153,79 @@ def cpu_baseline(spec, seed, budget_s: float, score: str = "cosine", k_e4m3: boo
             "selection_ms": t_sel * 1e3, "measured_s": round(measured, 2)}
 
 
+def bench_offload(spec, args, dev):
+    """Round workloads through a layer stack: resident (every layer's cache on
+    the GPU) against round offload (the layers above the watershed held per
+    round in pinned host memory, chosen rounds copied in after selection)."""
+    from sparse_kv_selection_amd import driver
+    if spec.n_rounds == 0:
+        sys.exit("--offload-layers needs a round workload (rounds_64k)")
+    L, w, T, n = args.offload_layers, args.watershed, spec.t_past, spec.bcp
+    off = W.round_offsets(T, spec.n_rounds, args.seed)
+    stack = driver.RoundOffloadStack(L, w, off, spec.b, spec.nkv, spec.d, n, device=dev)
+    caches, qs, krows, vrows = [], [], [], []
+    for layer in range(L):
+        case = W.make_case(spec, args.seed + 7919 * layer, device=dev)
+        stack.load_history(layer, case["k"], case["v"])
+        c = driver.KVCache(spec.b, spec.nkv, T + n, spec.d, device=dev)
+        c.k[:, :, :T].copy_(case["k"][:, :, :T])
+        c.v[:, :, :T].copy_(case["v"][:, :, :T])
+        c.advance(T)
+        caches.append(c)
+        qs.append(case["q"])
+        krows.append(case["k"][:, :, T:T + n].contiguous())
+        vrows.append(case["v"][:, :, T:T + n].contiguous())
+    off_dev = torch.tensor(off, dtype=torch.int32, device=dev)
+    plan = T // 4
+
+    def resident():
+        for c in caches:
+            c.length = T
+        return driver.layer_stack_step(qs, caches, krows, vrows, spec.nq_keep, plan, w,
+                                       round_off=off_dev, top_rounds=spec.top_rounds)
+
+    def offload():
+        return stack.step(qs, krows, vrows, spec.nq_keep, spec.top_rounds, plan)
+
+    def timed(fn, steps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    steps = max(3, min(args.steps, 20))
+    ms_res = timed(resident, steps)
+    ms_off = timed(offload, steps)
+    outs_o, _ = offload()
+    outs_r, _ = resident()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(outs_o, outs_r))
+    copy_ms = sum(s.elapsed_time(e) for s, e in stack.copy_events)
+    h2d = stack.last_h2d_bytes
+    result = {
+        "metric": "round-offload layer stack chunk ms (host-held upper layers) + H2D GB/s",
+        "value": round(ms_off, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": 2,
+        "ms_per_step": round(ms_off, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": f"{spec.name}: {_describe(spec)}", "layers": L, "watershed": w,
+                   "rounds_copied": len(stack.last_rounds)},
+        "resident_stack_ms": round(ms_res, 4),
+        "h2d_bytes_per_chunk": h2d,
+        "h2d_copy_ms": round(copy_ms, 4),
+        "h2d_gbps": round(h2d / (copy_ms * 1e-3) / 1e9, 2) if copy_ms > 0 else None,
+        "gpu_kv_bytes": stack.device_kv_bytes(), "resident_kv_bytes": stack.resident_kv_bytes(),
+        "gpu_kv_saved_frac": round(1 - stack.device_kv_bytes() / stack.resident_kv_bytes(), 4),
+        "outputs_equal_resident": same,
+        "timing": "wall clock over whole steps (the step waits on the host for the watershed's "
+                  "selection before it schedules the copies)",
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +242,10 @@ def main():
                     help="scoring: the method's cosine score or the dot-product baseline")
     ap.add_argument("--keys", default="dtype", choices=["dtype", "e4m3"],
                     help="keys the scoring pass reads: the cache dtype or an 8-bit E4M3 copy")
+    ap.add_argument("--offload-layers", type=int, default=0,
+                    help="round workloads: a stack of this many layers whose layers above the "
+                         "watershed keep their KV per round in pinned host memory")
+    ap.add_argument("--watershed", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
@@ -194,6 +271,8 @@ def main():
         return
 
     spec = W.spec(args.workload)
+    if args.offload_layers:
+        return bench_offload(spec, args, dev)
     rounds = spec.n_rounds > 0
     shape = qk.shape_of(spec, bsa=spec.t_past // 4 if rounds else spec.bsa)
     one_copy = sum(spec.b * h * r * spec.d * (2 if spec.dtype == "bf16" else 4)

@@ -185,6 +185,7 @@ class RoundOffloadStack:
         self.chosen_host = torch.empty((b, nkv, self.R), dtype=torch.uint8, pin_memory=True)
         self.last_h2d_bytes = 0
         self.last_rounds: List[int] = []
+        self.copy_events: List[tuple] = []  # (start, end) per upper layer, on the copy stream
 
     def load_history(self, layer: int, k: torch.Tensor, v: torch.Tensor):
         """Keys and values (b, nkv, >= T, d) of the T past positions of a layer."""
@@ -250,20 +251,24 @@ class RoundOffloadStack:
         need = self.chosen_host.reshape(-1, self.R).amax(dim=0)
         rounds = [r for r in range(self.R) if int(need[r])]
         done: List[torch.cuda.Event] = []
+        self.copy_events = []
         h2d = 0
         for i, layer in enumerate(range(w + 1, self.L)):
             st = self.stage[i % 2]
             with torch.cuda.stream(self.copy_stream):
                 if i >= 2:
                     self.copy_stream.wait_event(done[i - 2])  # that staging cache is free again
+                t0 = torch.cuda.Event(enable_timing=True)
+                t0.record(self.copy_stream)
                 blocks = self.host[i]
                 for r in rounds:  # one host-to-device copy per round
                     st[:, :, :, self.off[r]:self.off[r + 1]].copy_(blocks[r], non_blocking=True)
                     h2d += blocks[r].numel() * blocks[r].element_size()
                 st[0, :, :, T:T + n].copy_(k_rows[layer])
                 st[1, :, :, T:T + n].copy_(v_rows[layer])
-                staged = torch.cuda.Event()
+                staged = torch.cuda.Event(enable_timing=True)
                 staged.record(self.copy_stream)
+                self.copy_events.append((t0, staged))
             for t in (k_rows[layer], v_rows[layer]):
                 t.record_stream(self.copy_stream)
             compute.wait_event(staged)
