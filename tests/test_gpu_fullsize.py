@@ -102,3 +102,65 @@ def test_full_size(gpu, name):
         got_lse = np64(pipe.lse[bi:bi + 1])[:, heads][:, :, rows]
         assert np.abs(got_lse - lse_ref).max() <= 2e-3
         print(f"[full-size] {name} b{bi}: s_agg err {err:.2e}, attention err {err_o:.2e}", flush=True)
+
+
+VARIANTS_FULL = [("llama3b_32k", "cosine", True), ("long_128k", "cosine", True),
+                 ("decode_64x16k", "cosine", True), ("llama3b_32k", "dot", False)]
+
+
+@pytest.mark.parametrize("name,mode,e4m3", VARIANTS_FULL)
+def test_full_size_scoring_variants(gpu, name, mode, e4m3):
+    """The benchmarked scoring variants at full size: E4M3 key bytes (a KV
+    head's rows, bit-exact), scores of one sequence against the oracle on the
+    same keys, its key sets (boundary rule) and sampled attention rows."""
+    qk = gpu
+    dev = torch.device("cuda:0")
+    spec = W.spec(name)
+    seed = FULL[name]
+    print(f"[full-size variant] {name} {mode} e4m3={e4m3} seed {seed}", flush=True)
+    case = W.make_case(spec, seed, device=dev)
+    q, k, v = case["q"], case["k"], case["v"]
+    s = qk.shape_of(spec)
+    pipe = qk.Pipeline(s, device=dev, score_mode=mode, k_e4m3=e4m3)
+    if e4m3:
+        pipe.store_keys_e4m3(k)
+    pipe(q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed + 1)
+    bi = 0 if spec.b == 1 else int(rng.integers(spec.b))
+    qn, kn, vn = np64(q[bi:bi + 1]), np64(k[bi:bi + 1]), np64(v[bi:bi + 1])
+    if e4m3:
+        j0 = int(rng.integers(spec.nkv))
+        got8 = pipe.k8[bi, j0, :spec.t_past].cpu().numpy()
+        assert np.array_equal(got8, oracle.e4m3_encode(kn[0, j0, :spec.t_past]))
+        keys = oracle.scoring_keys_e4m3(kn[:, :, :spec.t_past])
+    else:
+        keys = kn
+    ref = oracle.pipeline(qn, kn, vn, spec.t_past, spec.nq_keep, spec.bsa, score=mode, k_e4m3=e4m3,
+                          with_attention=False)
+    agree = group_agreement(npi(pipe.q_idx[bi])[None], ref["qidx"], spec.group)[0]
+    assert agree.mean() >= 0.5
+    g_s = np64(pipe.s_agg[bi:bi + 1])
+    g_idx = npi(pipe.idx[bi])
+    if mode == "dot":
+        bound = np.matmul(np.abs(ref["q_group"]), np.swapaxes(np.abs(keys[:, :, :spec.t_past]), -1, -2)).max(axis=2)
+    for j in range(spec.nkv):
+        assert_sorted_unique(g_idx[j], spec.t_past)
+        if not agree[j]:
+            continue
+        err = np.abs(g_s[0, j] - ref["s_agg"][0, j])
+        if mode == "dot":
+            assert (err / bound[0, j]).max() <= 3e-5
+            tol = max(BOUNDARY_TOL, 3e-5 * float(bound[0, j].max()))
+        else:
+            assert err.max() <= 5e-5
+            tol = BOUNDARY_TOL
+        assert_set_within_boundary(g_idx[j], ref["kidx"][0, j], ref["s_agg"][0, j], s.n_sel,
+                                   tol=tol, what=f"kidx j{j}")
+    # sampled attention rows over the GPU's own key sets (attention reads bf16 keys)
+    sets = [[g_idx[j] for j in range(spec.nkv)]]
+    heads = rng.choice(spec.nq, size=min(4, spec.nq), replace=False)
+    rows = rng.choice(spec.bcp, size=min(8, spec.bcp), replace=False)
+    o_ref, _ = oracle.attention(qn, kn, vn, spec.t_past, sets, rows=rows, heads=heads)
+    got = np64(pipe.out[bi:bi + 1])[:, heads][:, :, rows]
+    assert np.abs(got - o_ref).max() <= ATTN_TOL[spec.dtype]
