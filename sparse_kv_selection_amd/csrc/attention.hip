@@ -441,58 +441,76 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   }
 }
 
-// Merge key-split partials, one wave per output row:
+// Merge key-split partials:
 //   O = sum_s w_s M_s P_s / sum_s w_s,  w_s = 2^(lse_s - max_s lse_s),
-// P_s the fp16 partial scaled by 1 / M_s.  Lane s < n_split (<= 64) holds split
-// s's (lse, M); every lane then loads its d-slots of all splits at once.
+// P_s the fp16 partial scaled by 1 / M_s.  A row's D fp16 values are covered
+// by D / 8 lanes with 16 bytes each, so one wave handles 512 / D consecutive
+// rows and each of its loads of one split reads 1 KiB contiguous.  Every lane
+// of a row reads that row's (lse, M) of all splits (same addresses within a
+// row: one request) and forms the weights itself.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const uint32_t* __restrict__ part_o,
                                                            const float2* __restrict__ part_ls,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse, int n_split,
                                                            long long rows) {
-  constexpr int PER = D / 128;  // fp16 pairs per lane
+  constexpr int LPR = D / 8;           // lanes per row
+  constexpr int RPW = 64 / LPR;        // rows per wave
+  constexpr int kBatch = 16;           // splits loaded together
   const int lane = threadIdx.x & 63;
-  const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float2 lm = lane < n_split ? part_ls[lane * rows + row] : float2{-INFINITY, 0.f};
-  const float mx = wave_max(lm.x);
-  const float w = (lm.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lm.x - mx);
-  const float wsum = wave_sum(w);
-  const float f = w * lm.y;  // weight of the scaled partial
-  float acc[2 * (PER > 0 ? PER : 1)];
-#pragma unroll
-  for (int e = 0; e < 2 * (PER > 0 ? PER : 1); ++e) acc[e] = 0.f;
-  constexpr int kBatch = 16;
-  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
-    uint32_t x[kBatch][PER > 0 ? PER : 1];
+  const long long row0 = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW;
+  const long long row = row0 + lane / LPR;
+  const int c = lane % LPR;            // this lane's 8 values: d = 8c .. 8c + 7
+  const bool live = row < rows;
+  const long long r = live ? row : rows - 1;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float mx = -INFINITY, wsum = 0.f;
+  // one batch of splits: (lse, M) and the partial words loaded together
+  auto batch = [&](int s0, bool find_max) {
+    float2 lm[kBatch];
+    u32x4 x[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int sidx = min(s0 + u, n_split - 1);
-      const uint32_t* src = part_o + (sidx * rows + row) * (D / 2);
-#pragma unroll
-      for (int e = 0; e < (PER > 0 ? PER : 1); ++e)
-        x[u][e] = (PER > 0 || lane < D / 2) ? src[lane + 64 * e] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float fu = s0 + u < n_split ? __shfl(f, s0 + u) : 0.f;
-#pragma unroll
-      for (int e = 0; e < (PER > 0 ? PER : 1); ++e) {
-        const f32x2 v = unpack_f16x2(x[u][e]);
-        acc[2 * e] += fu * v[0];
-        acc[2 * e + 1] += fu * v[1];
+      // a uniform branch: only the row's splits are read (no clamped repeats)
+      if (s0 + u < n_split) {
+        const long long sidx = s0 + u;
+        lm[u] = part_ls[sidx * rows + r];
+        x[u] = *reinterpret_cast<const u32x4*>(part_o + (sidx * rows + r) * (D / 2) + 4 * c);
       }
     }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (find_max) {
 #pragma unroll
-  for (int e = 0; e < (PER > 0 ? PER : 1); ++e) {
-    const int d = 2 * (lane + 64 * e);
-    if (PER > 0 || lane < D / 2)
-      *reinterpret_cast<uint32_t*>(out + row * D + d) = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      for (int u = 0; u < kBatch; ++u)
+        if (s0 + u < n_split) mx = fmaxf(mx, lm[u].x);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u >= n_split) break;
+      const float w = lm[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lm[u].x - mx);
+      wsum += w;
+      const float f = w * lm[u].y;  // weight of the scaled partial
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 v = unpack_f16x2(x[u][e]);
+        acc[2 * e] += f * v[0];
+        acc[2 * e + 1] += f * v[1];
+      }
+    }
+  };
+  if (n_split <= kBatch) {
+    batch(0, true);  // the usual case: one memory round trip
+  } else {
+    for (int s = 0; s < n_split; ++s)
+      mx = fmaxf(mx, part_ls[static_cast<long long>(s) * rows + r].x);
+    for (int s0 = 0; s0 < n_split; s0 += kBatch) batch(s0, false);
   }
-  if (lse && lane == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
+  if (!live) return;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + row * D + 8 * c) = o;
+  if (lse && c == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: one thread per packed query row, natural-base online softmax.
@@ -644,7 +662,8 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   else if (c.d == 256) e = run_bf16<256, 1, 4, 1>(p, grid, st);
   else return hipErrorInvalidValue;
   if (e != hipSuccess || pl.n_split == 1) return e;
-  const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4)), cblock(256);
+  const size_t rows_per_wg = 4 * (512 / c.d);  // 4 waves, 512 / d rows each
+  const dim3 cgrid(static_cast<unsigned>((rows + rows_per_wg - 1) / rows_per_wg)), cblock(256);
   if (c.d == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, st, p.part_o, p.part_ls,
                        static_cast<uint16_t*>(c.out), c.lse, pl.n_split, static_cast<long long>(rows));
