@@ -127,7 +127,6 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
   const int n_cand = keep_latest ? n_rounds - 1 : n_rounds;
   for (int r = tid; r < n_rounds; r += kRoundThreads) {
     const float sr = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
-    if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = sr;
     bool chosen = true;
     if (r < n_cand) {
       int rank = 0;
@@ -138,7 +137,6 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
       chosen = rank < top_r;
     }
     base[r] = chosen ? 1 : -1;
-    if (chosen_out) chosen_out[static_cast<size_t>(bj) * n_rounds + r] = chosen ? 1 : 0;
   }
   __syncthreads();
 
@@ -152,7 +150,6 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
     if (r < n_rounds) base[r] = base[r] > 0 ? running + ex : -1;
     running += tot;
   }
-  if (tid == 0) sel_len[bj] = min(running, ld_idx);
   __syncthreads();
 
   // 4. positions of the chosen rounds, ascending
@@ -165,6 +162,13 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
       if (o < ld_idx) out[o] = t;
     }
   }
+  // per-round outputs last (a global store issued before a barrier holds the
+  // barrier until it completes); base[r] >= 0 marks a chosen round
+  for (int r = tid; r < n_rounds; r += kRoundThreads) {
+    if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
+    if (chosen_out) chosen_out[static_cast<size_t>(bj) * n_rounds + r] = base[r] >= 0 ? 1 : 0;
+  }
+  if (tid == 0) sel_len[bj] = min(running, ld_idx);
 }
 
 }  // namespace

@@ -269,7 +269,6 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
     if (c == 0 && i < bcp) {
       const float sc = -dot / (fmaxf(sqrtf(n2), kEps) * mq_norm);
       sq[i] = sc;
-      if (sq_out) sq_out[static_cast<size_t>(bh) * bcp + i] = sc;
     }
   };
   if constexpr (RPT > 0) {
@@ -298,6 +297,11 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   } else {
     top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out);
   }
+  // SQ goes out last, coalesced from LDS (unchanged since the barrier above):
+  // a global store issued before a barrier would hold that barrier until the
+  // store completes
+  if (sq_out)
+    for (int i = tid; i < bcp; i += NT) sq_out[static_cast<size_t>(bh) * bcp + i] = sq[i];
 }
 
 // One wave per (b, j, n): mean over the group's heads of the unit n-th kept query.

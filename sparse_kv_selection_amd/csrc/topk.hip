@@ -395,8 +395,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __
 #pragma unroll
   for (int v = 0; v < kTopkWaves; ++v) off += v < wave ? wtot[v] : 0;
   const int ex = off + incl - c0 - c1;
-  *reinterpret_cast<int2*>(part + static_cast<size_t>(w) * kBins + 2 * tid) = int2{c0, c1};
-  *reinterpret_cast<int2*>(part + (static_cast<size_t>(nwg) + w) * kBins + 2 * tid) = int2{ex, ex + c0};
   h[2 * tid] = ex;  // now the bins' write cursors (each thread rewrites only its own bins)
   h[2 * tid + 1] = ex + c0;
   __syncthreads();
@@ -417,6 +415,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __
                  static_cast<size_t>(w) * (kTile / 2);
   const int nvalid = min(kTile, n - sl * kTile);  // slots [0, nvalid) are filled
   for (int i = tid; 2 * i < nvalid; i += kTopkThreads) pairs[i] = stage[i];
+  // the tile's histogram and prefix, stored after the last barrier (a store
+  // before a barrier holds the barrier until it completes)
+  *reinterpret_cast<int2*>(part + static_cast<size_t>(w) * kBins + 2 * tid) = int2{c0, c1};
+  *reinterpret_cast<int2*>(part + (static_cast<size_t>(nwg) + w) * kBins + 2 * tid) = int2{ex, ex + c0};
 }
 
 constexpr int kMaxSlices = 1024;
