@@ -40,7 +40,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 
 constexpr int kRoundThreads = 1024;
 constexpr int kRoundWaves = kRoundThreads / 64;
-constexpr int kRun = 16;  // consecutive scores per thread per pass
+constexpr int kRun = 16;        // consecutive scores per thread per pass (short rounds)
+constexpr int kWaveBatch = 8;   // loads in flight per lane (long rounds)
+constexpr int kRankThreads = 16;  // threads ranking one round
 
 // Order-preserving float <-> uint32 maps (for integer atomic max in LDS).
 __device__ __forceinline__ uint32_t okey(float x) {
@@ -96,47 +98,69 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
   for (int r = tid; r < n_rounds; r += kRoundThreads) rkey[r] = 0u;
   __syncthreads();
 
-  // 1. round maxima: each thread scans runs of kRun consecutive scores (all
-  //    loads of a run in flight), tracking the round it is in
-  for (int i0 = tid * kRun; i0 < t_past; i0 += kRoundThreads * kRun) {
-    float x[kRun];
+  // 1. round maxima.  Long rounds (at least 256 scores on average): one wave
+  //    per round, round-robin over the waves, coalesced loads (kWaveBatch x 64
+  //    consecutive scores in flight), a wave maximum and a plain store.  Short
+  //    rounds: each thread scans runs of kRun consecutive scores, tracking the
+  //    round it is in, with integer atomic maxima in LDS.
+  if (t_past >= 256 * n_rounds) {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < n_rounds; r += kRoundWaves) {
+      const int lo = so[r], hi = so[r + 1];
+      float m = -INFINITY;
+      for (int base = lo; base < hi; base += 64 * kWaveBatch) {
+        float x[kWaveBatch];
 #pragma unroll
-    for (int e = 0; e < kRun; ++e) x[e] = i0 + e < t_past ? row[i0 + e] : -INFINITY;
-    int lo = 0, hi = n_rounds - 1;  // round holding i0: largest r with so[r] <= i0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (so[mid] <= i0) lo = mid; else hi = mid - 1;
-    }
-    int r = lo;
-    float m = -INFINITY;
+        for (int u = 0; u < kWaveBatch; ++u) x[u] = row[min(base + 64 * u + lane, t_past - 1)];
 #pragma unroll
-    for (int e = 0; e < kRun; ++e) {
-      if (i0 + e >= t_past) break;
-      while (r + 1 < n_rounds && i0 + e >= so[r + 1]) {
-        if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
-        m = -INFINITY;
-        ++r;
+        for (int u = 0; u < kWaveBatch; ++u)
+          if (base + 64 * u + lane < hi) m = fmaxf(m, x[u]);
       }
-      m = fmaxf(m, x[e]);
+      m = wave_max(m);
+      if (lane == 0) rkey[r] = m == -INFINITY ? 0u : okey(m);
     }
-    if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
+  } else {
+    for (int i0 = tid * kRun; i0 < t_past; i0 += kRoundThreads * kRun) {
+      float x[kRun];
+#pragma unroll
+      for (int e = 0; e < kRun; ++e) x[e] = i0 + e < t_past ? row[i0 + e] : -INFINITY;
+      int lo = 0, hi = n_rounds - 1;  // round holding i0: largest r with so[r] <= i0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (so[mid] <= i0) lo = mid; else hi = mid - 1;
+      }
+      int r = lo;
+      float m = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < kRun; ++e) {
+        if (i0 + e >= t_past) break;
+        while (r + 1 < n_rounds && i0 + e >= so[r + 1]) {
+          if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
+          m = -INFINITY;
+          ++r;
+        }
+        m = fmaxf(m, x[e]);
+      }
+      if (m != -INFINITY) atomicMax(&rkey[r], okey(m));
+    }
   }
   __syncthreads();
 
-  // 2. chosen rounds by rank (ties: lower round id); the latest is always kept
+  // 2. chosen rounds by rank (ties: lower round id); the latest is always
+  //    kept.  kRankThreads threads count the better rounds of one round.
   const int n_cand = keep_latest ? n_rounds - 1 : n_rounds;
-  for (int r = tid; r < n_rounds; r += kRoundThreads) {
-    const float sr = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
-    bool chosen = true;
-    if (r < n_cand) {
-      int rank = 0;
-      for (int r2 = 0; r2 < n_cand; ++r2) {
+  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads / kRankThreads) {
+    const int r = r0 + tid / kRankThreads, part = tid % kRankThreads;
+    const int rr = r < n_rounds ? r : n_rounds - 1;
+    const float sr = rkey[rr] ? ofloat(rkey[rr]) : -INFINITY;
+    int better = 0;
+    if (rr < n_cand)
+      for (int r2 = part; r2 < n_cand; r2 += kRankThreads) {
         const float s2 = rkey[r2] ? ofloat(rkey[r2]) : -INFINITY;
-        rank += (s2 > sr) | ((s2 == sr) & (r2 < r));
+        better += (s2 > sr) | ((s2 == sr) & (r2 < rr));
       }
-      chosen = rank < top_r;
-    }
-    base[r] = chosen ? 1 : -1;
+    better = group_sum<kRankThreads>(better);
+    if (r < n_rounds && part == 0) base[r] = (rr >= n_cand || better < top_r) ? 1 : -1;
   }
   __syncthreads();
 
@@ -152,16 +176,21 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
   }
   __syncthreads();
 
-  // 4. positions of the chosen rounds, ascending
+  // 4. positions of the chosen rounds, ascending: the waves take the rounds
+  //    round-robin, and a chosen round's positions go out in coalesced stores
   int32_t* out = idx + static_cast<size_t>(bj) * ld_idx;
-  for (int r = 0; r < n_rounds; ++r) {
-    const int b0 = base[r];
-    if (b0 < 0) continue;
-    for (int t = so[r] + tid; t < so[r + 1]; t += kRoundThreads) {
-      const int o = b0 + (t - so[r]);
-      if (o < ld_idx) out[o] = t;
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < n_rounds; r += kRoundWaves) {
+      const int b0 = base[r];
+      if (b0 < 0) continue;
+      for (int t = so[r] + lane; t < so[r + 1]; t += 64) {
+        const int o = b0 + (t - so[r]);
+        if (o < ld_idx) out[o] = t;
+      }
     }
   }
+  __syncthreads();
   // per-round outputs last (a global store issued before a barrier holds the
   // barrier until it completes); base[r] >= 0 marks a chosen round
   for (int r = tid; r < n_rounds; r += kRoundThreads) {

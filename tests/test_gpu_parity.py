@@ -33,6 +33,9 @@ CASES = {
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
                                         top_rounds=4), 1004),
+    # rounds shorter than 256 positions on average: the per-thread scan
+    "rounds_short": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=48,
+                                        top_rounds=6), 1006),
 }
 
 _cache = {}
