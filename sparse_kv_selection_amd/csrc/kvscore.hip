@@ -49,22 +49,32 @@ struct ScoreArgs {
 // listing: the kept queries are L2-normalised, then averaged over the G heads
 // of the group), split into bf16 high and low parts in LDS.  Thread pair p =
 // (row n, 8-element chunk c); the CH threads of a row are adjacent lanes of
-// one wave, so a row norm is a shuffle sum.  The kept positions of the first
-// GB heads are loaded by load_pos before the caller issues its key loads.
-template <int D, int NQB>
+// one wave, so a row norm is a shuffle sum.
+//
+// Order of the memory trips: the kept positions, then the kept rows of the
+// first GB heads (issue), and only then the caller's first key blocks.  Loads
+// retire in issue order, so rows requested after the key blocks could not be
+// used before every one of those blocks had arrived (several microseconds at
+// the start of the pass, when every wave has its ring in flight).  Heads
+// beyond the first GB are loaded in build, behind the key blocks.
+template <int D, int NQB, int GB>
 struct GroupBuild {
   static constexpr int CH = D / 8;
   static constexpr int ROWS = NQB * 32;
   static constexpr int U = ROWS * CH / (64 * kScoreWaves);  // pairs per thread
-  static constexpr int GB = 4;                               // heads per batch
   static constexpr int LD = D + 8;                           // padded LDS row (bf16)
   static_assert(U >= 1 && (64 * kScoreWaves) % CH == 0, "pair layout");
 
-  int pos[U][GB];
+  u32x4 x[U][GB];
 
-  __device__ __forceinline__ void load_pos(const ScoreArgs& a, int bj, int g0) {
+  // kept rows of heads g0 .. g0 + GB - 1 (clamped to the last head: the loads
+  // are unconditional, so the wait before their use counts exactly them)
+  __device__ __forceinline__ void issue(const ScoreArgs& a, int bj, int g0) {
     const int b = bj / a.nkv, j = bj - b * a.nkv;
     const int32_t* qi = a.q_idx + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.nq_keep;
+    const uint16_t* qb = a.q + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.bcp * D;
+    const int c = threadIdx.x % CH;
+    int pos[U][GB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int n = min((static_cast<int>(threadIdx.x) + 64 * kScoreWaves * u) / CH, a.nq_keep - 1);
@@ -77,51 +87,55 @@ struct GroupBuild {
     // every index load goes out before the first one is used (the scheduler
     // would otherwise sink each load down to its use and wait on it there)
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg) {
+        const int g = min(g0 + gg, a.group - 1);
+        x[u][gg] = ld16(qb + (static_cast<size_t>(g) * a.bcp + pos[u][gg]) * D + 8 * c);
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // DOT: the kept rows enter unnormalised (dot-product scoring variant)
   template <bool DOT>
+  __device__ __forceinline__ void accumulate(const ScoreArgs& a, int g0, float (&acc)[U][8]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[2 * e] = bf16lo(x[u][gg][e]); v[2 * e + 1] = bf16hi(x[u][gg][e]); }
+        float inv = g0 + gg < a.group ? 1.0f : 0.f;
+        if constexpr (!DOT) {
+          float n2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) n2 += v[e] * v[e];
+#pragma unroll
+          for (int o = CH / 2; o > 0; o >>= 1) n2 += __shfl_xor(n2, o);
+          inv *= 1.0f / fmaxf(sqrtf(n2), kEps);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] += v[e] * inv;
+      }
+  }
+
+  // Completes the group queries from the rows of the first batch (already
+  // issued) and writes them to LDS; the caller then passes an LDS barrier.
+  template <bool DOT>
   __device__ __forceinline__ void build(const ScoreArgs& a, int bj, uint16_t* s_hi,
                                         uint16_t* s_lo) {
-    const int b = bj / a.nkv, j = bj - b * a.nkv;
-    const uint16_t* qb = a.q + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.bcp * D;
     const int c = threadIdx.x % CH;
     float acc[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
-    for (int g0 = 0; g0 < a.group; g0 += GB) {
-      if (g0 > 0) load_pos(a, bj, g0);
-      u32x4 x[U][GB];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int gg = 0; gg < GB; ++gg) {
-          const int g = min(g0 + gg, a.group - 1);
-          x[u][gg] = ld16(qb + (static_cast<size_t>(g) * a.bcp + pos[u][gg]) * D + 8 * c);
-        }
-      // all row loads in flight together (see load_pos)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int gg = 0; gg < GB; ++gg) {
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v[2 * e] = bf16lo(x[u][gg][e]); v[2 * e + 1] = bf16hi(x[u][gg][e]); }
-          float inv = g0 + gg < a.group ? 1.0f : 0.f;
-          if constexpr (!DOT) {
-            float n2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) n2 += v[e] * v[e];
-#pragma unroll
-            for (int o = CH / 2; o > 0; o >>= 1) n2 += __shfl_xor(n2, o);
-            inv *= 1.0f / fmaxf(sqrtf(n2), kEps);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[u][e] += v[e] * inv;
-        }
+    accumulate<DOT>(a, 0, acc);
+    for (int g0 = GB; g0 < a.group; g0 += GB) {
+      issue(a, bj, g0);
+      accumulate<DOT>(a, g0, acc);
     }
     const float inv_g = 1.0f / static_cast<float>(a.group);
 #pragma unroll
@@ -142,6 +156,14 @@ struct GroupBuild {
     }
   }
 };
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the global loads in flight (the key blocks of the ring).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Two E4M3 codes (bytes 2 SEL, 2 SEL + 1 of w) as a bf16 pair.  The hardware
 // decode to fp32 is exact, and so is keeping the upper half of the fp32
@@ -167,12 +189,12 @@ __device__ __forceinline__ int qofs(int s, int half) {
 template <int D, int NQB>
 constexpr int score_waves_per_simd() { return (D == 256 || NQB > 1) ? 1 : 2; }
 
-template <int D, int NQB, int STAGES, bool GROUPED, bool FP8, bool DOT>
+template <int D, int NQB, int STAGES, bool GROUPED, bool FP8, bool DOT, int GB>
 __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>())) void kvscore_bf16_kernel(ScoreArgs a) {
   constexpr int NS = D / 16;  // k-steps per key
   constexpr int NL = FP8 ? D / 32 : NS;  // 16-byte loads per key
   static_assert(GROUPED || (!FP8 && !DOT), "variants form their group queries");
-  using GBuild = GroupBuild<D, NQB>;
+  using GBuild = GroupBuild<D, NQB, GB>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   // a workgroup's waves all score one (b, KV head)
@@ -192,7 +214,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
   float* out = a.s_agg + static_cast<size_t>(bj) * a.t_past;
 
   GBuild gb;
-  if constexpr (GROUPED) gb.load_pos(a, bj, 0);  // kept positions first: a dependent trip
+  if constexpr (GROUPED) gb.issue(a, bj, 0);  // kept positions, then their rows
 
   u32x4 buf[STAGES][NL];
   auto load_block = [&](int blk, u32x4* dst) {
@@ -201,19 +223,27 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
 #pragma unroll
     for (int s = 0; s < NL; ++s) dst[s] = ld16(src + 32 * s);
   };
-  // First blocks in flight before the query fragments are built.  The loads
+  // First blocks in flight while the query fragments are built.  The loads
   // are unconditional (a wave with fewer blocks re-reads its first one, or a
-  // clamped row): behind a branch, the wait before the kept positions' first
-  // use would have to assume that no key load is in flight and wait for all.
+  // clamped row): behind a branch, the wait before the kept rows' first use
+  // would have to assume that no key load is in flight and wait for all.
+  // Grouped: one block before the kept rows are used, the rest of the ring
+  // after.  Every key request in flight on the chip delays the kept rows
+  // (they queue behind the key lines in the memory pipeline), and the rows
+  // gate every wave's first product; one block per wave measured best.
+  constexpr int kEarly = GROUPED ? 1 : STAGES - 1;
 #pragma unroll
-  for (int i = 0; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
+  for (int i = 0; i < kEarly; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
+  __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 qhi[NQB][NS], qlo[NQB][NS];
   if constexpr (GROUPED) {
     __shared__ __align__(16) uint16_t s_hi[GBuild::ROWS * GBuild::LD];
     __shared__ __align__(16) uint16_t s_lo[GBuild::ROWS * GBuild::LD];
     gb.template build<DOT>(a, bj, s_hi, s_lo);
-    __syncthreads();
+#pragma unroll
+    for (int i = kEarly; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
+    lds_barrier();
     if (nblk == 0) return;
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
@@ -369,19 +399,30 @@ __global__ __launch_bounds__(256) void kvscore_f32_kernel(ScoreCall c) {
   c.s_agg[static_cast<size_t>(bj) * c.t_past + t] = c.dot ? m : m / fmaxf(sqrtf(n2), kEps);
 }
 
+template <int D, int NQB, int STAGES, int GB>
+void launch_variant(const ScoreArgs& a, bool fp8, bool dot, dim3 grid, hipStream_t st) {
+  const dim3 block(64 * kScoreWaves);
+  if (!fp8 && !dot)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, false, GB>), grid, block, 0, st, a);
+  else if (!fp8)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, true, GB>), grid, block, 0, st, a);
+  else if (!dot)
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, false, GB>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, true, GB>), grid, block, 0, st, a);
+}
+
+// Heads per batch of kept-row loads: every head of groups up to 8 in the
+// first batch (the one issued ahead of the key blocks).
 template <int D, int NQB, int STAGES>
 void launch_grid(const ScoreArgs& a, bool fp8, bool dot, dim3 grid, hipStream_t st) {
-  const dim3 block(64 * kScoreWaves);
   if (a.q_group)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false, false, false>), grid, block, 0, st, a);
-  else if (!fp8 && !dot)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, false>), grid, block, 0, st, a);
-  else if (!fp8)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, false, true>), grid, block, 0, st, a);
-  else if (!dot)
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, false, false, false, 1>), grid,
+                       dim3(64 * kScoreWaves), 0, st, a);
+  else if (a.group <= 4)
+    launch_variant<D, NQB, STAGES, 4>(a, fp8, dot, grid, st);
   else
-    hipLaunchKernelGGL((kvscore_bf16_kernel<D, NQB, STAGES, true, true, true>), grid, block, 0, st, a);
+    launch_variant<D, NQB, STAGES, 8>(a, fp8, dot, grid, st);
 }
 
 template <int D, int NQB>
