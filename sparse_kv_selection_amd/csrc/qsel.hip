@@ -50,11 +50,30 @@ template <> struct Raw8<float> {
 
 __device__ __forceinline__ uint32_t okey(float x) { return order_key(x); }
 
+// Bins of the selection histogram (equal width between the chunk's smallest and
+// largest SQ; NQ-th key found by one wave's crossing search over them).
+constexpr int kQselBins = 512;
+
+// Sum over the lanes of a wave that share lane % CH (CH = 8, 16 or 32): DPP
+// rotation by 8 inside each 16-lane row, then the gfx950 lane swaps between
+// 16-lane rows and between the 32-lane halves.  Every lane gets the sum.
+template <int CH>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  static_assert(CH == 8 || CH == 16 || CH == 32, "row group width");
+  if constexpr (CH <= 8) x += dpp_f<0x128>(x);  // row_ror:8
+  if constexpr (CH <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One wave sorts P = 64 * E packed keys descending (bitonic network); lane l
 // holds positions [l * E, (l + 1) * E).  Key = (score key << 32) | ~position,
 // so larger scores come first and equal scores keep the lower position first.
 template <int E>
-__device__ void wave_sort_desc(uint64_t* v) {
+__device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
   const int lane = threadIdx.x & 63;
   constexpr int P = 64 * E;
 #pragma unroll
@@ -93,7 +112,7 @@ __device__ void wave_sort_desc(uint64_t* v) {
 
 // Wave 0 of the block: top-NQ positions of sq[0..bcp) by decreasing score.
 template <int E>
-__device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* out) {
+__device__ __forceinline__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* out) {
   const int lane = threadIdx.x & 63;
   uint64_t v[E];
 #pragma unroll
@@ -112,7 +131,7 @@ __device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* ou
 // Top-NQ positions of sq[0..bcp) by decreasing key K(i) = (order key of
 // sq[i] << 32) | ~i: larger scores first, equal scores at the lower position
 // first (keys are unique, so the result is exact and deterministic).
-//   1. histogram over 2048 equal-width bins between the smallest and the
+//   1. histogram over kQselBins equal-width bins between the smallest and the
 //      largest score (the bin is monotone in the score); the boundary bin B
 //      holds the NQ-th largest key, `above` keys lie in higher bins;
 //   2. the positions of the higher bins (list A, fewer than NQ) and of bin B
@@ -120,34 +139,32 @@ __device__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* ou
 //   3. each entry of A is ranked among A and each of C among C by counting
 //      larger keys, 16 threads per entry; A's ranks are final, C's are offset
 //      by |A| and kept while below NQ - |A|.
-// scratch: hist_words(2048) + 256 + bcp + 4 ints.  Every thread of the block
-// calls this.
+// scratch: hist_words(kQselBins) + 256 + bcp + 4 ints, its histogram and
+// counters cleared by select_clear before the barrier that precedes this call;
+// red: each wave's smallest and largest SQ, written before that barrier.
+// Every thread of the block calls this.  (Inlined: as a called function it
+// needed a scratch slot per lane, and a kernel with scratch waits for its
+// allocation at launch.)
 template <int NT>
-__device__ void top_positions_select(const float* sq, int* scratch, int bcp, int nq_keep,
-                                     int32_t* out) {
-  constexpr int kB = 2048, kWaves = NT / 64, TPP = 16;
+__device__ __forceinline__ void select_clear(int* scratch, int bcp) {
+  for (int i = threadIdx.x; i < hist_words(kQselBins); i += NT) scratch[i] = 0;
+  if (threadIdx.x < 2) scratch[hist_words(kQselBins) + 256 + bcp + threadIdx.x] = 0;
+}
+template <int NT>
+__device__ __forceinline__ void top_positions_select(const float* sq, int* scratch, int bcp, int nq_keep,
+                                                     int32_t* out, const float (*red)[NT / 64]) {
+  constexpr int kB = kQselBins, kWaves = NT / 64, TPP = 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* hist = scratch;
   int* la = hist + hist_words(kB);
   int* lc = la + 256;
   int* cnt = lc + bcp;  // |A|, |C|, B, above
-  __shared__ float red[2][kWaves];
   auto key = [&](int i) {
     return (static_cast<uint64_t>(okey(sq[i])) << 32) | static_cast<uint32_t>(~i);
   };
-  float mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < bcp; i += NT) {
-    mn = fminf(mn, sq[i]);
-    mx = fmaxf(mx, sq[i]);
-  }
-  mn = group_reduce<64>(mn, [](float a, float b) { return fminf(a, b); });
-  mx = group_reduce<64>(mx, [](float a, float b) { return fmaxf(a, b); });
-  if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
-  for (int i = tid; i < hist_words(kB); i += NT) hist[i] = 0;
-  if (tid < 2) cnt[tid] = 0;
-  __syncthreads();
+  float mn = red[0][0], mx = red[1][0];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) { mn = fminf(mn, red[0][w]); mx = fmaxf(mx, red[1][w]); }
+  for (int w = 1; w < kWaves; ++w) { mn = fminf(mn, red[0][w]); mx = fmaxf(mx, red[1][w]); }
   float scale = static_cast<float>(kB) / (mx - mn);
   if (!(scale < INFINITY)) scale = 0.f;  // all scores equal: one bin
   auto bin = [&](int i) { return min(max(static_cast<int>((sq[i] - mn) * scale), 0), kB - 1); };
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
   extern __shared__ float smem[];
   float* part = smem;                // [NRL][D] (or the selection scratch, if larger)
-  float* mq = part + (E > 0 ? NRL * D : max(NRL * D, hist_words(2048) + 256 + bcp + 4));  // [D]
+  float* mq = part + (E > 0 ? NRL * D : max(NRL * D, hist_words(kQselBins) + 256 + bcp + 4));  // [D]
   float* sq = mq + D;                // [bcp]
   const int tid = threadIdx.x;
   const int c = tid % CH, rl = tid / CH;
@@ -239,13 +256,19 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
       for (int e = 0; e < 8; ++e) acc[e] += x[e];
     }
   }
+  // column sums of the wave's rows in registers, one partial row per wave
+  constexpr int W = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[rl * D + 8 * c + e] = acc[e];
+  for (int e = 0; e < 8; ++e) acc[e] = rowgroup_sum<CH>(acc[e]);
+  if (lane < CH)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave * D + 8 * c + e] = acc[e];
   __syncthreads();
-  // mean query: S lanes per column, NRL / S partials each, then a shuffle sum
+  // mean query: S lanes per column, W / S partials each, then a shuffle sum
   for (int col = tid / S; col < D; col += NT / S) {
     float sum = 0.f;
-    for (int r = tid % S; r < NRL; r += S) sum += part[r * D + col];
+    for (int r = tid % S; r < W; r += S) sum += part[r * D + col];
     sum = group_sum<S>(sum);
     if (tid % S == 0) mq[col] = sum / static_cast<float>(bcp);
   }
@@ -259,24 +282,47 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   }
   const float mq_norm = fmaxf(sqrtf(group_sum<CH>(m2)), kEps);
 
-  // SQ per row: the CH lanes of a row sit in one wave
+  // SQ per row: the CH lanes of a row sit in one wave.  mn / mx: the
+  // smallest and largest SQ this lane wrote (for the selection histogram)
+  float mn = INFINITY, mx = -INFINITY;
+  auto sq_of = [&](float dot, float n2) {
+    const float v = -dot / (fmaxf(sqrtf(n2), kEps) * mq_norm);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+    return v;
+  };
   auto score_row = [&](int i, const float* x) {
     float dot = 0.f, n2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { dot += x[e] * m8[e]; n2 += x[e] * x[e]; }
     dot = group_sum<CH>(dot);
     n2 = group_sum<CH>(n2);
-    if (c == 0 && i < bcp) {
-      const float sc = -dot / (fmaxf(sqrtf(n2), kEps) * mq_norm);
-      sq[i] = sc;
-    }
+    if (c == 0 && i < bcp) sq[i] = sq_of(dot, n2);
   };
   if constexpr (RPT > 0) {
+    // the row sums of all RPT rows first; then lane c of the row group
+    // finishes row u = c (+ CH, ...): one square root and one division per
+    // lane instead of RPT (the VALU is the bound of this phase)
+    float dots[RPT], n2s[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       float x[8];
       rows[u].get(x);
-      score_row(u * NRL + rl, x);
+      float dot = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { dot += x[e] * m8[e]; n2 += x[e] * x[e]; }
+      dots[u] = group_sum<CH>(dot);
+      n2s[u] = group_sum<CH>(n2);
+    }
+#pragma unroll
+    for (int u0 = 0; u0 < RPT; u0 += CH) {
+      const int u = u0 + c;
+      float dot = 0.f, n2 = 1.f;
+#pragma unroll
+      for (int v = 0; v < RPT; ++v)
+        if (v == u) { dot = dots[v]; n2 = n2s[v]; }
+      const int i = u * NRL + rl;
+      if (u < RPT && i < bcp) sq[i] = sq_of(dot, n2);
     }
   } else {
     for (int i0 = 0; i0 < bcp; i0 += NRL) {
@@ -290,12 +336,19 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
       score_row(i, x);
     }
   }
+  __shared__ float red[2][W];
+  if constexpr (E == 0) {
+    mn = group_reduce<64>(mn, [](float a, float b) { return fminf(a, b); });
+    mx = group_reduce<64>(mx, [](float a, float b) { return fmaxf(a, b); });
+    if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
+    select_clear<NT>(reinterpret_cast<int*>(part), bcp);  // the partials are consumed
+  }
   __syncthreads();
   int32_t* out = q_idx + static_cast<size_t>(bh) * nq_keep;
   if constexpr (E > 0) {
     if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out);
   } else {
-    top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out);
+    top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out, red);
   }
   // SQ goes out last, coalesced from LDS (unchanged since the barrier above):
   // a global store issued before a barrier would hold that barrier until the
@@ -361,7 +414,7 @@ void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bc
     const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
     hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
   } else {
-    const size_t part = std::max<size_t>(static_cast<size_t>(NRL) * D, hist_words(2048) + 256 + bcp + 4);
+    const size_t part = std::max<size_t>(static_cast<size_t>(NRL) * D, hist_words(kQselBins) + 256 + bcp + 4);
     const size_t shm = sizeof(float) * (part + D + bcp);
     hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
   }
