@@ -47,10 +47,44 @@ struct TopkShared {
   int hist[kHistWords];
   uint32_t cand[kCand];
   uint32_t wsum[kTopkWaves];
+  int wtot[kTopkWaves];
   float red_min[kTopkWaves], red_max[kTopkWaves];
-  int bin, above, cnt, need;
+  int bin, above, nbin, cnt, need;
   uint32_t tau;
 };
+
+// Boundary bin of a histogram held two bins per thread (thread t: bins 2t and
+// 2t + 1, counts c0 and c1): the bin b with count(bins > b) < need <=
+// count(bins >= b), for 1 <= need <= total.  The whole block takes part: one
+// wave prefix sum, the waves' totals through LDS, then the one thread whose
+// bin it is writes (bin, above, its count).  Every thread calls this; the
+// results are visible after the second barrier.
+__device__ __forceinline__ void block_crossing(int c0, int c1, int need, int* wtot, int* bin,
+                                               int* above, int* count) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c0 + c1)));
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int below = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int v = wtot[w];
+    total += v;
+    below += w < wave ? v : 0;
+  }
+  const int above1 = total - below - incl;  // bins > 2t + 1
+  const int above0 = above1 + c1;           // bins > 2t
+  if (above1 < need && need <= above1 + c1) {
+    *bin = 2 * t + 1;
+    *above = above1;
+    *count = c1;
+  } else if (above0 < need && need <= above0 + c0) {
+    *bin = 2 * t;
+    *above = above0;
+    *count = c0;
+  }
+  __syncthreads();
+}
 
 // Exact threshold among the LDS candidate list: the need-th largest key.
 // Writes sh.tau and sh.need (copies of the threshold still to take).
@@ -259,8 +293,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __r
     else bins[e >> 1] = static_cast<uint32_t>(b);
   }
   __syncthreads();
-  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin, &sh.above);
-  __syncthreads();
+  block_crossing(sh.hist[hpad(2 * tid)], sh.hist[hpad(2 * tid + 1)], k, sh.wtot, &sh.bin, &sh.above,
+                 &sh.nbin);
   const uint32_t B = static_cast<uint32_t>(min(max(sh.bin, 0), kBins - 1));
   const int need0 = k - sh.above;
 
@@ -424,7 +458,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __
 constexpr int kMaxSlices = 1024;
 
 struct SplitShared {
-  int hist[kHistWords];       // the row's level-1 histogram
   int hist2[kHistWords];      // radix levels over bin B's key range
   alignas(16) uint32_t ckey[kSplitCand];
   int cpos[kSplitCand];
@@ -432,10 +465,11 @@ struct SplitShared {
   int seg_off[kMaxSlices];        // ... found at this offset in tile t's sorted pairs
   uint32_t wsum[kTopkWaves];
   int red[2][kTopkWaves];
-  int bin[2], above[2];
+  int bin[2], above[2], nb;
   uint32_t tau;
   int need;
 };
+
 
 // Sum over the block of (a, b); every thread gets the totals.
 __device__ __forceinline__ void block_sum2(int& a, int& b, int (*red)[kTopkWaves]) {
@@ -469,43 +503,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
 
   // Its own tile and the row's tile histograms are requested together
   // (batches of 8 tiles, addresses clamped so that a batch is branch-free).
+  // Thread t sums bins 2t and 2t + 1 over the tiles (all, and those before
+  // its own).
   float xo[IPT];
   const uint32_t vo = load_tile<IPT, VEC>(s, p0, n, xo);
-  constexpr int U = kBins / kTopkThreads;
+  static_assert(kBins == 2 * kTopkThreads, "two bins per thread");
   constexpr int kBatch = 8;
-  int total[U], before[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) { total[u] = 0; before[u] = 0; }
+  int total[2] = {0, 0}, before[2] = {0, 0};
   for (int s0 = 0; s0 < slices; s0 += kBatch) {
-    int v[kBatch][U];
+    int2 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
+      v[i] = *reinterpret_cast<const int2*>(prow + static_cast<size_t>(min(s0 + i, slices - 1)) * kBins +
+                                            2 * tid);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[i][u] = prow[static_cast<size_t>(min(s0 + i, slices - 1)) * kBins + tid + kTopkThreads * u];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = s0 + i < slices ? v[i][u] : 0;
-        total[u] += c;
-        before[u] += s0 + i < sl ? c : 0;
-      }
+    for (int i = 0; i < kBatch; ++i) {
+      const int c0 = s0 + i < slices ? v[i].x : 0, c1 = s0 + i < slices ? v[i].y : 0;
+      total[0] += c0;
+      total[1] += c1;
+      before[0] += s0 + i < sl ? c0 : 0;
+      before[1] += s0 + i < sl ? c1 : 0;
+    }
   }
 
   // 1. boundary bin B of the row; bins above it in earlier tiles
-#pragma unroll
-  for (int u = 0; u < U; ++u) sh.hist[hpad(tid + kTopkThreads * u)] = total[u];
-  __syncthreads();
-  if (wave == 0) wave_crossing<kBins / 64>(sh.hist, k, &sh.bin[0], &sh.above[0]);
-  __syncthreads();
+  block_crossing(total[0], total[1], k, sh.red[0], &sh.bin[0], &sh.above[0],
+                 &sh.nb);
   const uint32_t B = static_cast<uint32_t>(min(max(sh.bin[0], 0), kBins - 1));
   int need = k - sh.above[0];
-  const int nb = sh.hist[hpad(B)];
+  const int nb = sh.nb;
   int above_before = 0, unused = 0;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    above_before += static_cast<uint32_t>(tid + kTopkThreads * u) > B ? before[u] : 0;
+  for (int u = 0; u < 2; ++u)
+    above_before += static_cast<uint32_t>(2 * tid + u) > B ? before[u] : 0;
 
   // 2. bin B's pairs of every tile -> LDS when they fit (else every visit
   //    below reads them from the workspace)
