@@ -75,7 +75,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // 64); every lane gets its group's sum.  Within 16 lanes the partners come
 // from DPP (lane xor 1, xor 2, then the mirrored lane of the 8- and the
 // 16-lane half, which after the earlier steps holds the other half's sum);
-// wider groups add cross-row shuffles.  Every lane of the wave must be active.
+// wider groups add the gfx950 lane swaps (16-lane rows, then 32-lane halves),
+// which stay in the vector unit (no LDS round trip).  Every lane of the wave
+// must be active.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
@@ -83,6 +85,20 @@ __device__ __forceinline__ int dpp_i(int x) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+// op(v, v of lane ^ X) for X = 16 or 32, op commutative: the swap hands every
+// lane its own value and its partner's (in an order that depends on the lane).
+template <int X, typename T, typename Op>
+__device__ __forceinline__ T swap_op(T v, Op op) {
+  static_assert(sizeof(T) == 4 && (X == 16 || X == 32), "32-bit values, xor 16 or 32");
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__builtin_bit_cast(T, static_cast<uint32_t>(r[0])), __builtin_bit_cast(T, static_cast<uint32_t>(r[1])));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__builtin_bit_cast(T, static_cast<uint32_t>(r[0])), __builtin_bit_cast(T, static_cast<uint32_t>(r[1])));
+  }
 }
 template <int W, typename T, typename Op>
 __device__ __forceinline__ T group_reduce(T v, Op op) {
@@ -99,8 +115,8 @@ __device__ __forceinline__ T group_reduce(T v, Op op) {
   if constexpr (W >= 4) v = op(v, step(v, q2{}));
   if constexpr (W >= 8) v = op(v, step(v, hm{}));
   if constexpr (W >= 16) v = op(v, step(v, rm{}));
-  if constexpr (W >= 32) v = op(v, __shfl_xor(v, 16));
-  if constexpr (W >= 64) v = op(v, __shfl_xor(v, 32));
+  if constexpr (W >= 32) v = swap_op<16>(v, op);
+  if constexpr (W >= 64) v = swap_op<32>(v, op);
   return v;
 }
 template <int W, typename T>
@@ -156,15 +172,9 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return group_reduce<64>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // 16-byte global load through the vector path.
