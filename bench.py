@@ -40,10 +40,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # followed by the shared device header): once either changes, the figure no
 # longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "334e491514733e2b", 69903300),
-    ("llama3b_32k", "attention"): ("attention.hip", "9ee16bf2aabeee42", 72672164),
-    ("long_128k", "kvscore"): ("kvscore.hip", "334e491514733e2b", 277083343),
-    ("long_128k", "attention"): ("attention.hip", "9ee16bf2aabeee42", 122577116),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 69909709),
+    ("llama3b_32k", "attention"): ("attention.hip", "b6fc9e5d2641e894", 72670925),
+    ("long_128k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 277107712),
+    ("long_128k", "attention"): ("attention.hip", "b6fc9e5d2641e894", 122586317),
 }
 
 
