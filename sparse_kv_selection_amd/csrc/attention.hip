@@ -165,10 +165,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_bf16_kernel(AttnParams p
   // entries are loaded one tile ahead of the data loads that use them.
   int krow[IPW];
   auto rows_of = [&](int t, int* rr) {
-    if (t < npt) {  // uniform
+    const int k0 = (pt0 + t) * kKeyTile;  // uniform
+    if (t < npt && k0 + kKeyTile <= n_past) {  // uniform: a whole past tile, no clamp
+      // entries at a wave-uniform base plus the lane's fixed row offset
+      const int32_t* it = IDX ? idx + k0 : nullptr;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) rr[i] = IDX ? it[static_cast<uint32_t>(trow[i])] : k0 + trow[i];
+    } else if (t < npt) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const int kk = min((pt0 + t) * kKeyTile + trow[i], n_past - 1);
+        const int kk = min(k0 + trow[i], n_past - 1);
         rr[i] = IDX ? idx[kk] : kk;
       }
     } else {
