@@ -121,6 +121,36 @@ def test_qsel_ties_keep_lower_positions(gpu, bcp):
     assert np.array_equal(npi(q_idx), want)
 
 
+# Every layout of the query-selection kernel: d = 64 / 128 / 256 (8, 16, 32
+# lanes per row), chunks held in registers four or eight rows per thread or
+# read twice (bcp beyond eight rows per thread), the one-wave sort (bcp <= 64)
+# and the 64- and 256-thread workgroups of short chunks.
+QSEL_LAYOUTS = [(64, 8), (64, 40), (64, 500), (64, 900), (64, 1100), (128, 16), (128, 60),
+                (128, 450), (128, 1000), (256, 2), (256, 7), (256, 100), (256, 200), (256, 260)]
+
+
+@pytest.mark.parametrize("d,bcp", QSEL_LAYOUTS)
+def test_qsel_layouts(gpu, d, bcp):
+    qk = gpu
+    spec = W.spec("llama3b_32k", nq=4, nkv=2, d=d, t_past=64, bcp=bcp,
+                  nq_keep=min(32, bcp), bsa=16)
+    s = qk.shape_of(spec)
+    case = W.make_case(spec, 2000 + d + bcp)
+    q = case["q"]
+    q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=torch.int32, device=_dev())
+    sq = torch.empty((s.b, s.nq, bcp), dtype=torch.float32, device=_dev())
+    qk.qk_qsel(s, q.to(_dev()), q_idx, sq, None)
+    torch.cuda.synchronize()
+    want_idx, want_sq = oracle.select_queries(np64(q), s.nq_keep)
+    assert max_abs(sq, want_sq) <= 1e-5
+    gi = npi(q_idx)
+    for b in range(s.b):
+        for h in range(s.nq):
+            assert_set_within_boundary(gi[b, h], want_idx[b, h], want_sq[b, h], s.nq_keep,
+                                       what=f"d{d} bcp{bcp} h{h}")
+            assert np.all(np.diff(want_sq[b, h][gi[b, h]]) <= BOUNDARY_TOL)
+
+
 # --------------------------------------------------------------------------
 # stage 2: scoring pass, fed the oracle's group queries
 # --------------------------------------------------------------------------
