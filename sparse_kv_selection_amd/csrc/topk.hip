@@ -179,7 +179,8 @@ __device__ __forceinline__ uint32_t load_tile(const float* s, int base, int n, f
 // in gmask (above the threshold) and the first elements of emask (equal to
 // it) while fewer than `need` equal elements have been taken in the whole row.
 // (base_gt, base_eq) count the elements of earlier tiles and are advanced by
-// this tile's totals.  Every thread of the block calls this.
+// this tile's totals.  Every thread of the block calls this, once, as the
+// kernel's last step (wsum is not released for reuse).
 template <int ITEMS>
 __device__ void write_picks(uint32_t gmask, uint32_t emask, int base, int need, int k,
                             int32_t* out, uint32_t* wsum, int& base_gt, int& base_eq) {
@@ -205,7 +206,6 @@ __device__ void write_picks(uint32_t gmask, uint32_t emask, int base, int need, 
     woff += w < wave ? v : 0u;
     tot += v;
   }
-  __syncthreads();  // wsum is reused by the next call
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint32_t ex = woff + pre[m];
