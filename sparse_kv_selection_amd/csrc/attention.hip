@@ -568,10 +568,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // faster than two blocks and one wave per SIMD (the accumulators of two
 // blocks overflow the architectural registers and shuttle through AGPRs).
 constexpr int kNB128 = 1;
-// Waves per workgroup at d = 128: eight (256 rows, one workgroup per CU, two
-// waves per SIMD), so that a K/V tile in LDS serves twice the rows of a
-// four-wave workgroup and each CU copies half as many tiles (measured: 2-3 %
-// faster at llama3b_32k, equal at 128K past).
+// Waves per workgroup at d = 128 when a KV head has more than 128 query rows:
+// eight (256 rows, one workgroup per CU, two waves per SIMD), so that a K/V
+// tile in LDS serves twice the rows of a four-wave workgroup and each CU
+// copies half as many tiles (measured: 2-3 % faster at llama3b_32k, equal at
+// 128K past).  Fewer rows (decode) keep four waves: there the waves past the
+// rows only help copy tiles, and eight were 8 % slower.
 constexpr int kWaves128 = 8;
 
 struct Plan {
@@ -582,15 +584,17 @@ Plan make_plan(int b, int nq, int nkv, int d, int bcp, int n_past_max) {
   Plan pl{};
   const int G = nq / nkv;
   const int M = G * bcp;
-  pl.waves = d == 128 ? kWaves128 : 4;
+  pl.waves = d == 128 && M > 128 ? kWaves128 : 4;
   pl.nb = d == 128 ? kNB128 : 1;
   pl.rows = pl.waves * pl.nb * 32;
   pl.n_qtiles = (M + pl.rows - 1) / pl.rows;
   const int past_tiles = (n_past_max + kKeyTile - 1) / kKeyTile;
   const long long base = static_cast<long long>(pl.n_qtiles) * b * nkv;
-  // key splits fill the resident slots (256 CUs x workgroups per CU) without
+  // key splits fill the resident slots (256 CUs x workgroups per CU: one for
+  // d = 256, two row blocks per wave or eight waves, else two) without
   // spilling into a second, mostly idle round; at least 4 key tiles per split
-  const long long slots = 256LL * ((d == 256 || pl.nb == 2 || pl.waves == 8) ? 1 : 2);  // WGs per CU
+  const long long wg_per_cu = (d == 256 || pl.nb == 2 || pl.waves == 8) ? 1 : 2;
+  const long long slots = 256LL * wg_per_cu;
   long long ns = slots / base;
   const long long max_split = past_tiles / 4 > 1 ? past_tiles / 4 : 1;
   if (ns > max_split) ns = max_split;
@@ -668,7 +672,8 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t st) {
   }
   const int grid = pl.n_qtiles * c.b * c.nkv * pl.n_split;
   hipError_t e;
-  if (c.d == 128) e = run_bf16<128, kNB128, kWaves128, 1>(p, grid, st);
+  if (c.d == 128 && pl.waves == kWaves128) e = run_bf16<128, kNB128, kWaves128, 1>(p, grid, st);
+  else if (c.d == 128) e = run_bf16<128, kNB128, 4, 2>(p, grid, st);
   else if (c.d == 64) e = run_bf16<64, 1, 4, 2>(p, grid, st);
   else if (c.d == 256) e = run_bf16<256, 1, 4, 1>(p, grid, st);
   else return hipErrorInvalidValue;
