@@ -40,10 +40,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # followed by the shared device header): once either changes, the figure no
 # longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 69909914),
-    ("llama3b_32k", "attention"): ("attention.hip", "349f889e76f6b451", 72664576),
-    ("long_128k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 277106688),
-    ("long_128k", "attention"): ("attention.hip", "349f889e76f6b451", 122619290),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 69909709),
+    ("llama3b_32k", "attention"): ("attention.hip", "fd00fc37fa3ea8bb", 71477043),
+    ("long_128k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 277107098),
+    ("long_128k", "attention"): ("attention.hip", "fd00fc37fa3ea8bb", 122580582),
 }
 
 
