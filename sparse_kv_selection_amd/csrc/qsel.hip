@@ -224,7 +224,8 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   constexpr int NRL = NT / CH;       // rows handled at once
   constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
   extern __shared__ float smem[];
-  float* part = smem;                // [NRL][D] (or the selection scratch, if larger)
+  float* part = smem;                // [NT / 64][D] column partials, one row per wave (room for
+                                     // NRL rows), then the selection scratch
   float* mq = part + (E > 0 ? NRL * D : max(NRL * D, hist_words(kQselBins) + 256 + bcp + 4));  // [D]
   float* sq = mq + D;                // [bcp]
   const int tid = threadIdx.x;
