@@ -33,6 +33,19 @@ template <> struct Raw8<uint16_t> {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo(w[e]); x[2 * e + 1] = bf16hi(w[e]); }
   }
+  // sum of squares of the 8 values: packed bf16 dot products (exact products,
+  // fp32 sums; pairs taken by shuffles, not by a bit cast of one element)
+  __device__ __forceinline__ float sumsq() const {
+    const bf16x8 v = as_bf16x8(w);
+    float n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1),
+                                               __builtin_shufflevector(v, v, 0, 1), 0.f, false);
+    n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3),
+                                         __builtin_shufflevector(v, v, 2, 3), n2, false);
+    n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5),
+                                         __builtin_shufflevector(v, v, 4, 5), n2, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7),
+                                           __builtin_shufflevector(v, v, 6, 7), n2, false);
+  }
   __device__ __forceinline__ void zero() { w = u32x4{}; }
 };
 template <> struct Raw8<float> {
@@ -44,6 +57,12 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void get(float* x) const {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  }
+  __device__ __forceinline__ float sumsq() const {
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) n2 += a[e] * a[e] + b[e] * b[e];
+    return n2;
   }
   __device__ __forceinline__ void zero() { a = f32x4{}; b = f32x4{}; }
 };
@@ -309,9 +328,10 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
     for (int u = 0; u < RPT; ++u) {
       float x[8];
       rows[u].get(x);
-      float dot = 0.f, n2 = 0.f;
+      float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { dot += x[e] * m8[e]; n2 += x[e] * x[e]; }
+      for (int e = 0; e < 8; ++e) dot += x[e] * m8[e];
+      const float n2 = rows[u].sumsq();
       dots[u] = group_sum<CH>(dot);
       n2s[u] = group_sum<CH>(n2);
     }
