@@ -64,8 +64,8 @@ class PromptRunner:
     ``step`` runs one chunk (or, with one query, one decode step): it appends
     the chunk's key and value rows, runs selection and attention with the
     positions before the chunk as the past, and returns the chunk's output
-    (b, nq, n, d).  With ``record`` the (start, index list) of every step is
-    kept in ``history``."""
+    (b, nq, n, d).  With ``record`` every step's (start, index list, kept
+    query positions, query scores, key scores) are kept in ``history``."""
 
     def __init__(self, cache: KVCache, nq: int, nq_keep: int, bsa: int, score_mode: str = "cosine",
                  scale: float = 0.0, record: bool = False):
@@ -86,7 +86,9 @@ class PromptRunner:
             pipe.k8 = self.cache.k8
         out = pipe(q.contiguous(), self.cache.k, self.cache.v)
         if self.record:
-            self.history.append((self.cache.length, pipe.idx[..., :shape.n_sel].clone()))
+            t = self.cache.length
+            self.history.append((t, pipe.idx[..., :shape.n_sel].clone(), pipe.q_idx.clone(),
+                                 pipe.sq.clone(), pipe.s_agg[..., :t].clone()))
         self.cache.advance(n)
         self.last = pipe
         return out

@@ -6,8 +6,8 @@ import torch
 
 import oracle
 import workloads as W
-from parity import (ATTN_TOL, assert_set_within_boundary, assert_sorted_unique, group_agreement,
-                    max_abs, np64, npi)
+from parity import (ATTN_TOL, assert_set_within_boundary, max_abs, np64, npi, staged_attention,
+                    staged_selection)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,9 +51,10 @@ def test_prompt_full_budget_is_causal_attention(gpu):
 
 @pytest.mark.parametrize("e4m3", [False, True])
 def test_prompt_chunks_against_oracle(gpu, e4m3):
-    """Limited budget: every step's kept queries and key set agree with the
-    oracle's step (near-boundary swaps only), and every step's output equals
-    the oracle's attention over the GPU's own key sets."""
+    """Limited budget, every step compared stage by stage: kept queries
+    against the oracle's run of the step, then the oracle's key scores, key
+    selection and attention on the GPU's own kept queries and key sets, for
+    every KV group and every row of the step."""
     from sparse_kv_selection_amd import driver
     P, n_dec, bcp, bsa = 640, 2, 256, 150
     (q, k, v), = _sequence(P + n_dec, 3002)
@@ -61,33 +62,26 @@ def test_prompt_chunks_against_oracle(gpu, e4m3):
     cache = driver.KVCache(1, NKV, P + n_dec, D_HEAD, device=_dev(), e4m3=e4m3)
     run = driver.PromptRunner(cache, NQ, 16, bsa=bsa, record=True)
     starts = list(range(0, P, bcp)) + list(range(P, P + n_dec))
-    outs, qidx = [], []
+    outs = []
     for t in starts:
         e = min(t + bcp, P) if t < P else t + 1
         if t < P:
             o = run.step(q[:, :, t:e], k[:, :, t:e], v[:, :, t:e])
         else:
             o = run.decode(q[:, :, t:e], k[:, :, t:e], v[:, :, t:e])
-        outs.append(np64(o))
-        qidx.append(npi(run.last.q_idx))
+        outs.append(o.clone())
     torch.cuda.synchronize()
-    _, steps = oracle.prompt_chunks(qn, kn, vn, bcp, 16, bsa, n_decode=n_dec, k_e4m3=e4m3)
-    assert len(steps) == len(starts) == len(run.history)
-    for i, (t, ref) in enumerate(zip(starts, steps)):
-        t_hist, idx = run.history[i]
-        idx = npi(idx)
+    assert len(run.history) == len(starts)
+    for i, t in enumerate(starts):
+        t_hist, idx, q_idx, sq, s_agg = run.history[i]
+        n = outs[i].shape[2]
+        keep = min(16, n) if t < P else 1
         assert t_hist == t and idx.shape[-1] == min(bsa, t)
-        e = outs[i].shape[2] + t
-        agree = group_agreement(qidx[i], ref["qidx"], NQ // NKV)
-        for j in range(NKV):
-            if t > 0:
-                assert_sorted_unique(idx[0, j], t)
-            if t > 0 and agree[0, j]:
-                assert_set_within_boundary(idx[0, j], ref["kidx"][0, j], ref["s_agg"][0, j],
-                                           min(bsa, t), what=f"step {i} j{j}")
-        sets = [[idx[0, j] for j in range(NKV)]]
-        o_ref, _ = oracle.attention(qn[:, :, t:e], kn, vn, t, sets)
-        assert np.abs(outs[i] - o_ref).max() <= ATTN_TOL["bf16"], (i, t)
+        qs = qn[:, :, t:t + n]
+        sets, st = staged_selection(qs, kn, t, keep, bsa, np64(sq), npi(q_idx), np64(s_agg),
+                                    npi(idx), k_e4m3=e4m3, what=f"step {i} at {t}")
+        err = staged_attention(qs, kn, vn, t, sets, outs[i], "bf16", what=f"step {i} at {t}")
+        print(f"[prompt] step {i} at {t}: {st}, attention {err:.2e}")
 
 
 def test_layer_stack_watershed_reuse(gpu):
@@ -114,17 +108,13 @@ def test_layer_stack_watershed_reuse(gpu):
     vn = [np64(v) for (_, _, v) in layers]
     ref_outs, _ = oracle.layer_stack(qn, kn, vn, t_past, 16, bsa, w)
     assert max_abs(outs[0], ref_outs[0]) <= ATTN_TOL["bf16"]
-    ref_w = oracle.pipeline(qn[w], kn[w], vn[w], t_past, 16, bsa, with_attention=False)
-    idx = npi(pipe.idx)
-    agree = group_agreement(npi(pipe.q_idx), ref_w["qidx"], NQ // NKV)
-    for j in range(NKV):
-        assert_sorted_unique(idx[0, j], t_past)
-        if agree[0, j]:
-            assert_set_within_boundary(idx[0, j], ref_w["kidx"][0, j], ref_w["s_agg"][0, j], bsa)
-    sets = [[idx[0, j] for j in range(NKV)]]
+    # the watershed's selection, stage by stage on its own kept queries; the
+    # layers above attend over it with their own rows
+    sets, st = staged_selection(qn[w], kn[w], t_past, 16, bsa, np64(pipe.sq), npi(pipe.q_idx),
+                                np64(pipe.s_agg), npi(pipe.idx), what="watershed")
     for layer in (w, w + 1):
-        o_ref, _ = oracle.attention(qn[layer], kn[layer], vn[layer], t_past, sets)
-        assert max_abs(outs[layer], o_ref) <= ATTN_TOL["bf16"], layer
+        staged_attention(qn[layer], kn[layer], vn[layer], t_past, sets, outs[layer], "bf16",
+                         what=f"layer {layer}")
     assert all(c.length == t_past + bcp for c in caches)
 
 
@@ -168,16 +158,12 @@ def test_round_offload_matches_resident_stack(gpu):
     qn = [np64(x) for x in qs]
     kn = [np64(k) for (_, k, _) in layers]
     vn = [np64(v) for (_, _, v) in layers]
-    ref = oracle.pipeline(qn[w], kn[w], vn[w], T, 16, 0, round_off=np.asarray(off), top_rounds=top,
-                          with_attention=False)
-    for j in range(NKV):
-        got = np.flatnonzero(chosen[0, j])
-        want = np.asarray(ref["rounds"][0][j])
-        sr = np.asarray(ref["s_round"][0, j], dtype=np.float64).copy()
-        sr[R - 1] = np.inf
-        assert_set_within_boundary(got, want, sr, top + 1, what=f"rounds j{j}")
-    idx, sl = npi(pipe.idx), npi(pipe.sel_len)
-    sets = [[idx[0, j, :sl[0, j]] for j in range(NKV)]]
+    sets, st = staged_selection(qn[w], kn[w], T, 16, T // 4, np64(pipe.sq), npi(pipe.q_idx),
+                                np64(pipe.s_agg), npi(pipe.idx), round_off=np.asarray(off),
+                                top_rounds=top, gpu_sel_len=npi(pipe.sel_len), what="watershed")
+    for j in range(NKV):   # the chosen-round mask names the same rounds as the index list
+        rounds_in_list = np.unique(np.searchsorted(off, sets[0][j], side="right") - 1)
+        assert np.array_equal(np.flatnonzero(chosen[0, j]), rounds_in_list)
     for layer in (w, w + 1, L - 1):
-        o_ref, _ = oracle.attention(qn[layer], kn[layer], vn[layer], T, sets)
-        assert max_abs(outs[layer], o_ref) <= ATTN_TOL["bf16"], layer
+        staged_attention(qn[layer], kn[layer], vn[layer], T, sets, outs[layer], "bf16",
+                         what=f"layer {layer}")
