@@ -50,7 +50,8 @@
  * one workspace concurrently (different streams) race.
  *
  * Execution: every call validates its arguments on the host, enqueues its
- * kernels on `stream` and returns without synchronising.  The library holds no
+ * kernels on `stream` and returns without synchronising.  Apart from the
+ * fixed scratch array of qk_sparse_attn_indexed_noalloc, the library holds no
  * mutable global state; calls on different streams are independent.
  *
  * Errors: validation happens before any launch; on error nothing is launched
@@ -77,7 +78,9 @@ typedef enum {
   QK_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned          */
   QK_ERR_WORKSPACE = 5,   /* ws_bytes smaller than qk_workspace_bytes         */
   QK_ERR_UNSUPPORTED = 6, /* head dim or size beyond what the kernels handle  */
-  QK_ERR_HIP = 7          /* the HIP runtime refused a launch                 */
+  QK_ERR_HIP = 7,         /* the HIP runtime refused a launch                 */
+  QK_ERR_SCRATCH_LIMIT = 8 /* more scratch needed than the library's fixed
+                              array holds (QK_NOALLOC_SCRATCH_BYTES)          */
 } qk_status;
 
 typedef enum { QK_F32 = 0, QK_BF16 = 1 } qk_dtype;
@@ -256,6 +259,27 @@ qk_status qk_sparse_attn_indexed(const qk_shape* s, const void* q, const void* k
                                  const void* v, const int32_t* idx, int32_t ld_idx,
                                  const int32_t* sel_len, void* out, float* lse,
                                  void* ws, size_t ws_bytes, qk_stream_t stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qk_sparse_attn_indexed with
+ * its key-split partials in a file-scope device array of
+ * QK_NOALLOC_SCRATCH_BYTES that the library owns, instead of a caller
+ * workspace.  The call allocates and frees nothing; its first call on a device
+ * looks up that device's copy of the array (each GPU the library runs on holds
+ * one until the process ends).  A shape whose attention needs more than
+ * QK_NOALLOC_SCRATCH_BYTES (qk_workspace_bytes(QK_OP_SPARSE_ATTN)) is rejected
+ * with QK_ERR_SCRATCH_LIMIT before anything is launched.  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (concurrent streams, or
+ * host threads) race and must be serialised by the caller.  Outputs, errors
+ * and arithmetic are those of qk_sparse_attn_indexed.  20 MiB covers every
+ * shape: the attention plan keeps (key splits x query rows) within the
+ * resident workgroup slots times the rows of one workgroup, at most 17.3 MB
+ * of partials. */
+#define QK_NOALLOC_SCRATCH_BYTES ((size_t)20 << 20)
+qk_status qk_sparse_attn_indexed_noalloc(const qk_shape* s, const void* q, const void* k,
+                                         const void* v, const int32_t* idx, int32_t ld_idx,
+                                         const int32_t* sel_len, void* out, float* lse,
+                                         qk_stream_t stream);
 
 /* Dense attention of the chunk over every past key plus itself causally (the
  * dense baseline of the QUOKA write-up's section 3 tables).  Same outputs and

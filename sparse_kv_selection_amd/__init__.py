@@ -31,7 +31,8 @@ SCORE_MODES = {"cosine": QK_SCORE_COSINE, "dot": QK_SCORE_DOT}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
             "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
             "qk_topk", "qk_round_select", "qk_gather", "qk_sparse_attn",
-            "qk_sparse_attn_indexed", "qk_dense_attn"]
+            "qk_sparse_attn_indexed", "qk_sparse_attn_indexed_noalloc", "qk_dense_attn"]
+QK_NOALLOC_SCRATCH_BYTES = 20 << 20    # the fixed scratch array of qk_sparse_attn_indexed_noalloc
 
 
 class QKError(RuntimeError):
@@ -106,6 +107,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
         "qk_sparse_attn": ([F, P, P, P, I, P, P, P, P, P, P, SZ, P], I),
         "qk_sparse_attn_indexed": ([F, P, P, P, P, I, P, P, P, P, SZ, P], I),
+        "qk_sparse_attn_indexed_noalloc": ([F, P, P, P, P, I, P, P, P, P], I),
         "qk_dense_attn": ([F, P, P, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
@@ -227,6 +229,15 @@ def qk_sparse_attn_indexed(shape, q, k, v, idx, ld_idx, sel_len, out, lse=None, 
     _check("qk_sparse_attn_indexed", load_library().qk_sparse_attn_indexed(
         _sh(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), ld_idx, _ptr(sel_len), _ptr(out),
         _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def qk_sparse_attn_indexed_noalloc(shape, q, k, v, idx, ld_idx, sel_len, out, lse=None,
+                                   stream=None):
+    """qk_sparse_attn_indexed with the library's fixed scratch array instead of
+    a workspace (no allocation; calls overlapping on one GPU race)."""
+    _check("qk_sparse_attn_indexed_noalloc", load_library().qk_sparse_attn_indexed_noalloc(
+        _sh(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), ld_idx, _ptr(sel_len), _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def qk_dense_attn(shape, q, k, v, out, lse=None, ws=None, ws_bytes=0, stream=None):

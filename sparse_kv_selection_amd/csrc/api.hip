@@ -109,6 +109,8 @@ const char* qk_status_string(qk_status s) {
     case QK_ERR_WORKSPACE: return "workspace smaller than qk_workspace_bytes";
     case QK_ERR_UNSUPPORTED: return "head dim or size not handled by the kernels";
     case QK_ERR_HIP: return "the HIP runtime refused a launch";
+    case QK_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the library's fixed array holds";
   }
   return "unknown status";
 }

@@ -205,3 +205,30 @@ def test_workspace_sizes():
     assert qk.topk_workspace_bytes(512, 16384) == 0                    # one workgroup per row
     assert qk.topk_workspace_bytes(512, 16388) == tiles(512 * 5, 4096)
     assert qk.topk_workspace_bytes(8, 4096) == 0
+
+
+def test_noalloc_scratch_covers_every_plan():
+    """The fixed scratch array of qk_sparse_attn_indexed_noalloc holds the
+    key-split partials of every shape the attention plan produces (host-side
+    sizes only), and the binding's constant is the header's."""
+    text = open(HEADER).read()
+    m = re.search(r"#define QK_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == qk.QK_NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for d in (64, 128, 256):
+        for nkv in (1, 2, 8):
+            for G in (1, 3, 8, 16):
+                for bcp in (1, 7, 64, 200, 256, 512, 1000, 4096):
+                    for b in (1, 3, 64):
+                        for t in (100, 5000, 32768, 131072, 500000):
+                            s = qk.Shape(b, nkv * G, nkv, d, bcp, t, t + bcp, 1, t, 0.0, qk.QK_BF16)
+                            worst = max(worst, qk.qk_workspace_bytes(s, "sparse_attn"))
+    assert 0 < worst <= qk.QK_NOALLOC_SCRATCH_BYTES, worst
+
+
+def test_noalloc_status():
+    assert "fixed array" in qk.qk_status_string(8)
+    lib = ctypes.CDLL(qk.LIB_PATH)
+    fn = lib.qk_sparse_attn_indexed_noalloc
+    fn.restype = ctypes.c_int32
+    assert fn(None, None, None, None, None, 0, None, None, None, None) == NULL
