@@ -149,8 +149,46 @@ def cpu_baseline(spec, seed, budget_s: float, score: str = "cosine", k_e4m3: boo
         sample = (f"full selection (all {spec.b * spec.nkv} KV heads, T={spec.t_past}) + attention "
                   f"of {done}/{rows_total} chunk rows x all {spec.nq} heads, scaled to the whole chunk")
     return {"value": est * 1e3, "unit": "ms per chunk", "cores": int(threads), "kind": "oracle",
-            "sample": sample, "host": platform.processor() or platform.machine(),
+            "sample": sample, "cpu_model": _cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
+            "threading": ("numpy fp64: the matrix products run on the BLAS thread pool "
+                          "(blas_threads); the per-row sorts and the per-head loops on one thread"),
             "selection_ms": t_sel * 1e3, "measured_s": round(measured, 2)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+CALIB_MODES = {  # qk_calib_matrix_rate modes (include/qk.h)
+    "constant_registers": 0, "random_registers": 1, "constant_lds": 2, "random_lds": 3,
+    "constant_lds_softmax": 6, "random_lds_softmax": 7}
+
+
+def matrix_ceiling(dev, iters: int = 2048) -> dict:
+    """TFLOP/s the attention's matrix-core instruction mix sustains on this GPU
+    (qk_calib_matrix_rate): near-constant against random operands, from
+    registers, from LDS, and with the softmax vector work.  Measured with
+    events around each call on the current stream, after one warm-up call."""
+    out = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+    flops = 256.0 * 8 * iters * 32 * 32768
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, mode in CALIB_MODES.items():
+        qk.qk_calib_matrix_rate(mode, iters // 4, out)
+        e0.record()
+        qk.qk_calib_matrix_rate(mode, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return res
 
 
 def bench_offload(spec, args, dev):
@@ -387,6 +425,13 @@ def main():
                      "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(spec.name, "attention"),
                      "algorithmic_flops": work["attn_flops"], "ms": round(stage_ms["attention"], 5)}
+    if spec.bcp > 1:
+        # the published peak stays the denominator; beside it, what the same
+        # instruction mix reaches on this GPU with random operands (power-bound)
+        ceil = matrix_ceiling(dev)
+        roof_attn["ceiling"] = {"tflops_random_operands": ceil["random_lds_softmax"],
+                                "frac": round(attn_tflops / ceil["random_lds_softmax"], 4),
+                                "calibration_tflops": ceil}
     dominant = roof_attn if stage_ms["attention"] >= stage_ms["kvscore"] else roof_score
 
     result = {
@@ -424,6 +469,13 @@ def main():
         result["dense_attention_ms"] = round(dms, 5)
         result["dense_attention_tflops"] = round(work["dense_flops"] / (dms * 1e-3) / 1e12, 1)
         result["chunk_vs_dense_attention"] = round(dms / ms, 3)
+        result["dense_over_sparse_attention"] = round(dms / stage_ms["attention"], 3)
+        if spec.bcp == 1:
+            # memory-bound decode: dense moves K and V, the method K once plus
+            # the selected K and V rows, so the chunk can beat dense attention
+            # by at most 2 / (1 + 2 BSA / T)
+            f = shape.n_sel / spec.t_past
+            result["decode_ceiling_vs_dense"] = round(2.0 / (1.0 + 2.0 * f), 3)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, args.seed, args.cpu_budget, args.score, e4m3)

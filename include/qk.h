@@ -288,6 +288,17 @@ qk_status qk_dense_attn(const qk_shape* s, const void* q, const void* k,
                         const void* v, void* out, float* lse, void* ws,
                         size_t ws_bytes, qk_stream_t stream);
 
+/* Measurement only (no step of the method): the matrix-core rate that the
+ * attention kernel's instruction mix sustains on this GPU.  256 workgroups of
+ * eight waves each run `iters` tiles of 32 32x32x16 bf16 products (the value
+ * and key products of one 64-key tile at d = 128).  mode bit 0: random bf16
+ * operands of magnitude about one (else near-constant); bit 1: operands read
+ * from LDS in the attention's layouts (else from registers); bit 2: each tile
+ * followed by the softmax vector work that feeds the next value products.
+ * Rate = 256 * 8 * iters * 32 * 32768 flops over the call's duration.
+ * out: device, 256 * 512 floats (written, meaningless). */
+qk_status qk_calib_matrix_rate(int32_t mode, int32_t iters, float* out, qk_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ SCORE_MODES = {"cosine": QK_SCORE_COSINE, "dot": QK_SCORE_DOT}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
             "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
             "qk_topk", "qk_round_select", "qk_gather", "qk_sparse_attn",
-            "qk_sparse_attn_indexed", "qk_sparse_attn_indexed_noalloc", "qk_dense_attn"]
+            "qk_sparse_attn_indexed", "qk_sparse_attn_indexed_noalloc", "qk_dense_attn",
+            "qk_calib_matrix_rate"]
 QK_NOALLOC_SCRATCH_BYTES = 20 << 20    # the fixed scratch array of qk_sparse_attn_indexed_noalloc
 
 
@@ -109,6 +110,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_sparse_attn_indexed": ([F, P, P, P, P, I, P, P, P, P, SZ, P], I),
         "qk_sparse_attn_indexed_noalloc": ([F, P, P, P, P, I, P, P, P, P], I),
         "qk_dense_attn": ([F, P, P, P, P, P, P, SZ, P], I),
+        "qk_calib_matrix_rate": ([I, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -244,6 +246,13 @@ def qk_dense_attn(shape, q, k, v, out, lse=None, ws=None, ws_bytes=0, stream=Non
     _check("qk_dense_attn", load_library().qk_dense_attn(
         _sh(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
         _stream(stream)))
+
+
+def qk_calib_matrix_rate(mode, iters, out, stream=None):
+    """Measurement only: the attention's matrix-core instruction mix on
+    near-constant or random operands (see include/qk.h)."""
+    _check("qk_calib_matrix_rate", load_library().qk_calib_matrix_rate(int(mode), int(iters),
+                                                                        _ptr(out), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libqk.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "qsel.hip", "kvscore.hip", "keys_e4m3.hip", "topk.hip", "gather_rounds.hip",
-           "attention.hip", "noalloc.hip"]
+           "attention.hip", "noalloc.hip", "calib.hip"]
 
 ARCH = os.environ.get("QK_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
