@@ -2,7 +2,7 @@
 the selected keys, on one MI355X.
 
 A step is the whole hot path over one chunk whose inputs are resident in HBM:
-    qk_qsel -> qk_kvscore_grouped -> qk_topk -> qk_sparse_attn_indexed
+    qk_select (qk_qsel -> qk_kvscore_grouped -> qk_topk in one call) -> qk_sparse_attn_indexed
 (the gather of the selected rows is fused into the attention's loads).
 Steps rotate over several copies of the inputs (more bytes than the 256 MB
 Infinity Cache), so each step streams its K and V from HBM.
@@ -359,7 +359,8 @@ def main():
     # (the launches are enqueued ahead, so host gaps between calls do not
     # count).  A stage reads the previous stage's outputs as they stand, which
     # are valid inputs of the same shape.
-    stages = (["store_keys"] if e4m3 else []) + ["qsel", "kvscore", "select", "attention"]
+    stages = ((["store_keys"] if e4m3 else []) + ["qsel", "kvscore", "select", "attention"]
+              + (["select_one_call"] if pipe.fused_select else []))
 
     def run_stage(name, c):
         if name == "store_keys":
@@ -372,6 +373,10 @@ def main():
                                   pipe.s_agg)
         elif name == "kvscore":
             qk.qk_kvscore_grouped(shape, c["q"], pipe.q_idx, c["k"], pipe.s_agg)
+        elif name == "select_one_call":
+            # qk_select: query selection, scoring (with the histogram the
+            # top-k starts from) and top-k in one call, as the timed step runs
+            pipe.select(c["q"], c["k"])
         elif name == "select":
             if rounds:
                 qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"],
@@ -446,6 +451,11 @@ def main():
         "scoring_gbps": round(score_gbs, 1), "scoring_frac_of_peak": round(score_gbs / HBM_PEAK_GBS, 4),
         "keys_scored_per_s": spec.b * spec.nkv * spec.t_past / (stage_ms["kvscore"] * 1e-3),
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        # the one-call selection less its query and scoring stages: what the
+        # top-k costs after a scoring pass that fills its histogram
+        "topk_in_one_call_ms": (round(stage_ms["select_one_call"] - stage_ms["qsel"]
+                                      - stage_ms["kvscore"], 5)
+                                if "select_one_call" in stage_ms else None),
         "chunks_per_s": round(1e3 / ms, 1),
     }
 

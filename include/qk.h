@@ -15,6 +15,8 @@
  *                   (the dtype, or 8-bit E4M3 keys)
  *   qk_keys_to_e4m3 store key rows as E4M3 bytes for the 8-bit scoring pass
  *   qk_topk         per-row top-k indices of fp32 scores (ascending order)
+ *   qk_select       qk_qsel + qk_kvscore_variant + qk_topk in one call, the
+ *                   scoring pass also counting what the top-k needs first
  *   qk_round_select round-granular variant: round score = max over the round,
  *                   keep the latest round plus the top rounds
  *   qk_gather       copy the selected K/V rows into dense buffers
@@ -110,7 +112,8 @@ typedef enum {
   QK_OP_ROUND_SELECT = 3,
   QK_OP_GATHER = 4,
   QK_OP_SPARSE_ATTN = 5,
-  QK_OP_DENSE_ATTN = 6
+  QK_OP_DENSE_ATTN = 6,
+  QK_OP_SELECT = 7
 } qk_op;
 
 /* [host] Version of this ABI (bumped on any incompatible change). */
@@ -208,6 +211,23 @@ qk_status qk_keys_to_e4m3(const qk_shape* s, const void* k, int32_t row0, int32_
 qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores,
                   int32_t ld_scores, int32_t* idx, int32_t ld_idx, void* ws,
                   size_t ws_bytes, qk_stream_t stream);
+
+/* The whole selection of one chunk (QUOKA write-up, section 2.1 Algorithm 1
+ * and section 2.3 listing: query sub-selection, scoring of every past key
+ * against the group queries, top-BSA keys per KV head) in one call: the
+ * results of qk_qsel (q_group not formed), then qk_kvscore_variant(key_format,
+ * mode), then qk_topk(rows = b * nkv, n = t_past, k = bsa) over s_agg, bit for
+ * bit.  Writes q_idx (b,nq,NQ), sq (b,nq,bcp) unless NULL, s_agg (b,nkv,T) and
+ * idx (b,nkv,ld_idx) with ld_idx >= min(bsa, T).  Where the top-k spreads a
+ * row over several workgroups (see qk_topk) and s->dtype is QK_BF16, the
+ * scoring pass also counts every row's scores into the histogram the top-k
+ * starts from, which saves the top-k its own counting pass.  Scratch:
+ * qk_workspace_bytes(QK_OP_SELECT) bytes (ws, 16-byte aligned; NULL allowed
+ * when that is 0).  Needs T >= 1 and bsa >= 1 (else QK_ERR_SHAPE); other
+ * limits and errors as the three calls. */
+qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key_format,
+                    int32_t mode, int32_t* q_idx, float* sq, float* s_agg, int32_t* idx,
+                    int32_t ld_idx, void* ws, size_t ws_bytes, qk_stream_t stream);
 
 /* Round-granular selection (Round Attention press release, sections 01-02).
  * round_off: (n_rounds + 1) int32, off[0] = 0, strictly increasing,

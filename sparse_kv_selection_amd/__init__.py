@@ -24,13 +24,13 @@ LIB_PATH = os.path.join(_HERE, "libqk.so")
 
 QK_F32, QK_BF16 = 0, 1
 OPS = {"qsel": 0, "kvscore": 1, "topk": 2, "round_select": 3, "gather": 4,
-       "sparse_attn": 5, "dense_attn": 6}
+       "sparse_attn": 5, "dense_attn": 6, "select": 7}
 QK_SCORE_COSINE, QK_SCORE_DOT = 0, 1    # qk_score_mode
 QK_KEYS_DTYPE, QK_KEYS_E4M3 = 0, 1      # qk_key_format
 SCORE_MODES = {"cosine": QK_SCORE_COSINE, "dot": QK_SCORE_DOT}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
             "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
-            "qk_topk", "qk_round_select", "qk_gather", "qk_sparse_attn",
+            "qk_topk", "qk_select", "qk_round_select", "qk_gather", "qk_sparse_attn",
             "qk_sparse_attn_indexed", "qk_sparse_attn_indexed_noalloc", "qk_dense_attn",
             "qk_calib_matrix_rate"]
 QK_NOALLOC_SCRATCH_BYTES = 20 << 20    # the fixed scratch array of qk_sparse_attn_indexed_noalloc
@@ -104,6 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_kvscore_variant": ([F, P, P, P, I, I, P, P], I),
         "qk_keys_to_e4m3": ([F, P, I, I, P, P], I),
         "qk_topk": ([I, I, I, P, I, P, I, P, SZ, P], I),
+        "qk_select": ([F, P, P, I, I, P, P, P, P, I, P, SZ, P], I),
         "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P, P], I),
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
         "qk_sparse_attn": ([F, P, P, P, I, P, P, P, P, P, P, SZ, P], I),
@@ -206,6 +207,18 @@ def qk_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws=None, ws_bytes=0, str
                                               ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def qk_select(shape, q, k, key_format, mode, q_idx, sq, s_agg, idx, ld_idx, ws=None, ws_bytes=0,
+              stream=None):
+    """qk_qsel + qk_kvscore_variant + qk_topk in one call.  ws=None: a
+    workspace of the required size is allocated for this call."""
+    mode = SCORE_MODES[mode] if isinstance(mode, str) else int(mode)
+    if ws is None:
+        ws, ws_bytes = _ws(shape, "select", q.device)
+    _check("qk_select", load_library().qk_select(
+        _sh(shape), _ptr(q), _ptr(k), int(key_format), mode, _ptr(q_idx), _ptr(sq), _ptr(s_agg),
+        _ptr(idx), ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def qk_round_select(shape, s_agg, n_rounds, round_off, top_r, keep_latest, idx, ld_idx,
                     sel_len, s_round=None, chosen=None, stream=None):
     _check("qk_round_select", load_library().qk_round_select(
@@ -282,11 +295,16 @@ class Pipeline:
     ``k_e4m3``: the scoring pass reads 8-bit E4M3 keys from ``k8``, which the
     caller fills with ``store_keys_e4m3`` as rows are appended to the cache
     (attention still reads the bf16 keys).  Both variants need ``fused_group``.
+
+    ``fused_select``: top-BSA selection (no rounds) with ``fused_group`` goes
+    through qk_select, one call for qsel, scoring and top-k; otherwise the
+    three calls are made one by one (same results, bit for bit).
     """
 
     def __init__(self, shape: Shape, device="cuda", n_rounds: int = 0, top_rounds: int = 0,
                  keep_latest: bool = True, fused_gather: bool = True, with_lse: bool = True,
-                 fused_group: bool = True, score_mode: str = "cosine", k_e4m3: bool = False):
+                 fused_group: bool = True, score_mode: str = "cosine", k_e4m3: bool = False,
+                 fused_select: bool = True):
         s = self.shape = shape
         if score_mode not in SCORE_MODES:
             raise ValueError("score_mode is 'cosine' or 'dot'")
@@ -296,6 +314,8 @@ class Pipeline:
         self.device = torch.device(device)
         self.n_rounds, self.top_rounds, self.keep_latest = n_rounds, top_rounds, keep_latest
         self.fused_gather, self.fused_group = fused_gather, fused_group
+        self.fused_select = (fused_select and fused_group and not n_rounds and s.t_past >= 1
+                             and s.bsa >= 1)
         f32, i32 = torch.float32, torch.int32
         dev = self.device
         self.q_idx = torch.empty((s.b, s.nq, s.nq_keep), dtype=i32, device=dev)
@@ -321,6 +341,8 @@ class Pipeline:
         self.lse = torch.empty((s.b, s.nq, s.bcp), dtype=f32, device=dev) if with_lse else None
         self.ws, self.ws_bytes = _ws(s, "sparse_attn", dev)
         self.topk_ws_bytes = 0 if n_rounds else topk_workspace_bytes(s.b * s.nkv, s.t_past)
+        self.select_ws, self.select_ws_bytes = (_ws(s, "select", dev) if self.fused_select
+                                                else (None, 0))
         self.topk_ws = (torch.empty(self.topk_ws_bytes, dtype=torch.uint8, device=dev)
                         if self.topk_ws_bytes else None)
         self.k8 = (torch.empty((s.b, s.nkv, s.kv_cap, s.d), dtype=torch.uint8, device=dev)
@@ -347,6 +369,12 @@ class Pipeline:
 
     def select(self, q, k, round_off=None):
         s = self.shape
+        if self.fused_select:
+            qk_select(s, q, self.k8 if self.k_e4m3 else k,
+                      QK_KEYS_E4M3 if self.k_e4m3 else QK_KEYS_DTYPE, self.score_mode, self.q_idx,
+                      self.sq, self.s_agg, self.idx, self.ld_idx, self.select_ws,
+                      self.select_ws_bytes)
+            return
         self.score(q, k)
         if self.n_rounds:
             qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds,

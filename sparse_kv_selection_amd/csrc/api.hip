@@ -59,7 +59,8 @@ qk_status check_ws(const qk_shape* s, int32_t op, const void* ws, size_t ws_byte
 
 qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
                          const int32_t* q_idx, const void* k, float* s_agg, qk_stream_t stream,
-                         bool k_e4m3 = false, bool dot = false) {
+                         bool k_e4m3 = false, bool dot = false, bool check_only = false,
+                         int* hist = nullptr) {
   qk_status st = check_shape(s);
   if (st != QK_OK) return st;
   if (!k || !s_agg) return QK_ERR_NULL;
@@ -90,7 +91,35 @@ qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
   c.nq_keep = s->nq_keep;
   c.k_e4m3 = k_e4m3;
   c.dot = dot;
+  c.hist = hist;
+  if (check_only) return QK_OK;
   return hip_status(qk::launch_kvscore(c, hs(stream)));
+}
+
+qk_status qsel_check(const qk_shape* s, const void* q, const int32_t* q_idx, const float* sq,
+                     const float* q_group) {
+  qk_status st = check_shape(s);
+  if (st != QK_OK) return st;
+  if (!q || !q_idx) return QK_ERR_NULL;
+  if (s->nq_keep < 1 || s->nq_keep > s->bcp || s->nq_keep > 256) return QK_ERR_SHAPE;
+  if (!aligned16(q) || (q_group && !aligned16(q_group)) || !aligned4(q_idx) || (sq && !aligned4(sq)))
+    return QK_ERR_ALIGN;
+  return QK_OK;
+}
+
+// qk_select: the scoring pass fills the rows' level-1 histograms (bf16, and
+// only where the top-k spreads a row over several workgroups).
+inline bool select_row_hist(const qk_shape* s) {
+  return is_bf16(s) && qk::topk_uses_row_hist(s->b * s->nkv, s->t_past, s->bsa);
+}
+size_t select_ws_bytes(const qk_shape* s) {
+  if (s->bsa >= s->t_past) return 0;  // every key kept: nothing to count
+  return qk::topk_workspace_bytes(s->b * s->nkv, s->t_past, select_row_hist(s));
+}
+// Bytes at the start of the qk_select workspace that the scoring pass
+// accumulates into (cleared by the query pass before it).
+size_t select_hist_bytes(const qk_shape* s) {
+  return static_cast<size_t>(s->b) * s->nkv * qk::kL1BinsHost * sizeof(int);
 }
 
 }  // namespace
@@ -120,6 +149,7 @@ size_t qk_workspace_bytes(const qk_shape* s, int32_t op) {
   if (op == QK_OP_QSEL || op == QK_OP_KVSCORE || op == QK_OP_ROUND_SELECT || op == QK_OP_GATHER)
     return 0;
   if (check_shape(s) != QK_OK) return 0;
+  if (op == QK_OP_SELECT) return s->t_past >= 1 && s->bsa >= 1 ? select_ws_bytes(s) : 0;
   if (op == QK_OP_SPARSE_ATTN || op == QK_OP_DENSE_ATTN)
     return qk::attn_workspace_bytes(is_bf16(s), s->b, s->nq, s->nkv, s->d, s->bcp,
                                     attn_past_max(s, op == QK_OP_DENSE_ATTN));
@@ -128,14 +158,10 @@ size_t qk_workspace_bytes(const qk_shape* s, int32_t op) {
 
 qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq, float* q_group,
                   qk_stream_t stream) {
-  qk_status st = check_shape(s);
+  const qk_status st = qsel_check(s, q, q_idx, sq, q_group);
   if (st != QK_OK) return st;
-  if (!q || !q_idx) return QK_ERR_NULL;
-  if (s->nq_keep < 1 || s->nq_keep > s->bcp || s->nq_keep > 256) return QK_ERR_SHAPE;
-  if (!aligned16(q) || (q_group && !aligned16(q_group)) || !aligned4(q_idx) || (sq && !aligned4(sq)))
-    return QK_ERR_ALIGN;
   return hip_status(qk::launch_qsel(is_bf16(s), q, q_idx, sq, q_group, s->b, s->nq, s->nkv, s->d,
-                                    s->bcp, s->nq_keep, hs(stream)));
+                                    s->bcp, s->nq_keep, nullptr, 0, hs(stream)));
 }
 
 qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k, float* s_agg,
@@ -188,7 +214,38 @@ qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32
     if (!aligned16(ws)) return QK_ERR_ALIGN;
     if (ws_bytes < need) return QK_ERR_WORKSPACE;
   }
-  return hip_status(qk::launch_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws, hs(stream)));
+  return hip_status(qk::launch_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws, false, hs(stream)));
+}
+
+qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key_format,
+                    int32_t mode, int32_t* q_idx, float* sq, float* s_agg, int32_t* idx,
+                    int32_t ld_idx, void* ws, size_t ws_bytes, qk_stream_t stream) {
+  qk_status st = qsel_check(s, q, q_idx, sq, nullptr);
+  if (st != QK_OK) return st;
+  if ((key_format != QK_KEYS_DTYPE && key_format != QK_KEYS_E4M3) ||
+      (mode != QK_SCORE_COSINE && mode != QK_SCORE_DOT))
+    return QK_ERR_UNSUPPORTED;
+  const bool e4m3 = key_format == QK_KEYS_E4M3, dot = mode == QK_SCORE_DOT;
+  st = kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, e4m3, dot, true);
+  if (st != QK_OK) return st;
+  if (s->t_past < 1 || s->bsa < 1) return QK_ERR_SHAPE;
+  const int rows = s->b * s->nkv, n = s->t_past, kk = n_sel_of(s);
+  if (ld_idx < kk) return QK_ERR_SHAPE;
+  if (n > qk::topk_max_row()) return QK_ERR_UNSUPPORTED;
+  if (!idx) return QK_ERR_NULL;
+  if (!aligned4(idx)) return QK_ERR_ALIGN;
+  st = check_ws(s, QK_OP_SELECT, ws, ws_bytes);
+  if (st != QK_OK) return st;
+  const bool row_hist = select_row_hist(s);
+  int* hist = row_hist ? static_cast<int*>(ws) : nullptr;
+  hipError_t e = qk::launch_qsel(is_bf16(s), q, q_idx, sq, nullptr, s->b, s->nq, s->nkv, s->d,
+                                 s->bcp, s->nq_keep, hist, row_hist ? select_hist_bytes(s) : 0,
+                                 hs(stream));
+  if (e != hipSuccess) return QK_ERR_HIP;
+  st = kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, e4m3, dot, false, hist);
+  if (st != QK_OK) return st;
+  return hip_status(qk::launch_topk(rows, n, s->bsa, s_agg, n, idx, ld_idx, ws, row_hist,
+                                    hs(stream)));
 }
 
 qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,

@@ -41,6 +41,7 @@ struct ScoreArgs {
   const int32_t* q_idx;    // (b, nq, nq_keep) kept positions
   const void* k;           // (b, nkv, kv_cap, d) bf16, or E4M3 bytes
   float* s_agg;
+  int* hist;               // (b * nkv, kL1Bins) zeroed level-1 histograms, or nullptr
   int nkv, group, bcp, t_past, kv_cap, nq_keep;
   int blocks_per_bj, wgs_per_bj;
 };
@@ -213,6 +214,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
                    (static_cast<size_t>(bj) * a.kv_cap * D + (FP8 ? 16 : 8) * half) * (FP8 ? 1 : 2);
   float* out = a.s_agg + static_cast<size_t>(bj) * a.t_past;
 
+  // Histogram of the scores written, over the level-1 bins of the selection
+  // that follows: counted in LDS, added to the row's histogram at the end
+  // (one atomic per bin the workgroup touched).
+  __shared__ int lh[kL1Bins];
+  const bool with_hist = a.hist != nullptr;  // uniform
+  if (with_hist)
+    for (int i = threadIdx.x; i < kL1Bins; i += 64 * kScoreWaves) lh[i] = 0;
+
   GBuild gb;
   if constexpr (GROUPED) gb.issue(a, bj, 0);  // kept positions, then their rows
 
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
 #pragma unroll
     for (int i = kEarly; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
     lds_barrier();
-    if (nblk == 0) return;
+    if (nblk == 0 && !with_hist) return;  // (with the histogram, every wave meets its barrier)
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
       int row = mb * 32 + col;
@@ -257,7 +266,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
       }
     }
   } else {
-    if (nblk == 0) return;
+    if (with_hist) lds_barrier();  // the cleared histogram before any count
+    if (nblk == 0 && !with_hist) return;
     const float* qg = a.q_group + static_cast<size_t>(bj) * a.nq_keep * D;
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
@@ -329,12 +339,15 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
       for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[mb][r]);
     m = fmaxf(m, __shfl_xor(m, 32));
     const int key = blk * kBlock + col;
-    if constexpr (DOT) {
-      if (half == 0 && key < a.t_past) out[key] = m;
-    } else {
+    float v = m;
+    if constexpr (!DOT) {
       n2 += __shfl_xor(n2, 32);
       // m / max(|k|, eps) as m * rsqrt(max(|k|^2, eps^2))
-      if (half == 0 && key < a.t_past) out[key] = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+      v = m * __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+    }
+    if (half == 0 && key < a.t_past) {
+      out[key] = v;
+      if (with_hist) atomicAdd(&lh[l1_bin(order_key(v))], 1);
     }
   };
 
@@ -347,6 +360,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
       const int nxt = m + STAGES - 1;
       if (nxt < nblk) load_block(block_of(nxt), buf[(i + STAGES - 1) % STAGES]);
       score_block(block_of(m), buf[i]);
+    }
+  }
+  if (with_hist) {
+    lds_barrier();
+    int* gh = a.hist + static_cast<size_t>(bj) * kL1Bins;
+    for (int i = threadIdx.x; i < kL1Bins; i += 64 * kScoreWaves) {
+      const int c = lh[i];
+      if (c) atomicAdd(gh + i, c);
     }
   }
 }
@@ -434,6 +455,7 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   a.q_idx = c.q_idx;
   a.k = c.k;
   a.s_agg = c.s_agg;
+  a.hist = c.hist;
   a.nkv = c.nkv;
   a.group = c.nq / c.nkv;
   a.bcp = c.bcp;

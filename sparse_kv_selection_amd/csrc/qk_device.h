@@ -172,6 +172,36 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Level-1 bins of order keys for top-k selection over scores (2048 bins),
+// monotone in the key, so that every bin above the one holding the k-th
+// largest score is selected whole.  Each sign gets 1024 bins: 64 per binade
+// of |x| over [2^-8, 2^(1022/64 - 8)) (about 0.0039 to 250: cosine scores and
+// dot products of unit-scale vectors), one bin for the smaller magnitudes
+// next to zero and one for the larger ones (and NaN) at the end.  The top bits
+// of the key alone would spend most bins on exponents that such scores never
+// reach and put a tenth of a row into one bin.  The scoring pass can fill the
+// histogram of its rows in these bins for the selection that follows it.
+constexpr int kL1Bins = 2048;
+constexpr int kL1Shift = 17;         // key bits below a bin: 23 - 6 mantissa bits
+constexpr int kL1FineBase = 119 << 6;  // (exponent, top 6 mantissa bits) of 2^-8
+__device__ __forceinline__ int l1_bin(uint32_t key) {
+  const bool pos = key >= 0x80000000u;
+  const uint32_t mag = pos ? (key & 0x7fffffffu) : (0x7fffffffu - key);  // bits of |x|
+  const int v = static_cast<int>(mag >> kL1Shift) - kL1FineBase;
+  const int i = v < 0 ? 0 : min(v + 1, 1023);
+  return pos ? 1024 + i : 1023 - i;
+}
+// The keys of level-1 bin b: [*lo, *hi].
+__device__ __forceinline__ void l1_bin_range(int b, uint32_t* lo, uint32_t* hi) {
+  const bool pos = b >= 1024;
+  const int i = pos ? b - 1024 : 1023 - b;
+  const uint32_t mlo = i == 0 ? 0u : static_cast<uint32_t>(kL1FineBase + i - 1) << kL1Shift;
+  const uint32_t mhi =
+      i == 1023 ? 0x7fffffffu : (static_cast<uint32_t>(kL1FineBase + i) << kL1Shift) - 1u;
+  *lo = pos ? (0x80000000u | mlo) : (0x7fffffffu - mhi);
+  *hi = pos ? (0x80000000u | mhi) : (0x7fffffffu - mlo);
+}
+
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) {
   return group_reduce<64>(v, [](float a, float b) { return fmaxf(a, b); });

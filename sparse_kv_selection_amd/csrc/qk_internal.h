@@ -6,9 +6,12 @@
 
 namespace qk {
 
-// Query sub-selection + group aggregation.
+// Query sub-selection + group aggregation.  zero: nullptr, or zero_bytes (a
+// multiple of 16) of 16-byte aligned memory that the kernel also clears (the
+// histograms of the scoring pass that follows).
 hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group,
-                       int b, int nq, int nkv, int d, int bcp, int nq_keep, hipStream_t st);
+                       int b, int nq, int nkv, int d, int bcp, int nq_keep, int* zero,
+                       size_t zero_bytes, hipStream_t st);
 
 // Key scoring pass.  q_group == nullptr: the group queries are formed from
 // (q, q_idx) inside the scoring kernel.
@@ -22,6 +25,9 @@ struct ScoreCall {
   int b, nq, nkv, d, bcp, t_past, kv_cap, nq_keep;
   bool k_e4m3 = false;  // k holds E4M3 bytes (bf16 queries, grouped only)
   bool dot = false;     // dot-product scoring (grouped only)
+  // bf16 only: nullptr, or (b * nkv, kL1Bins) int32, zeroed, to which the pass
+  // adds every row's histogram of its scores over the level-1 bins
+  int* hist = nullptr;
 };
 hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
 
@@ -33,10 +39,15 @@ hipError_t launch_keys_e4m3(bool bf16, const void* k, uint8_t* k8, int bnkv, int
 size_t kvscore_f32_lds_bytes(int d, int nq_keep, int group);
 
 // Per-row top-k, ascending indices.  ws: topk_workspace_bytes of scratch.
-size_t topk_workspace_bytes(int rows, int n);
+// row_hist (only where topk_uses_row_hist): the workspace starts with every
+// row's histogram over the level-1 bins (rows x kL1Bins int32), filled by the
+// scoring pass, and the top-k skips its own counting pass.
+size_t topk_workspace_bytes(int rows, int n, bool row_hist = false);
 int topk_max_row();  // longest row qk_topk supports
+bool topk_uses_row_hist(int rows, int n, int k);
+constexpr int kL1BinsHost = 2048;  // the level-1 bins (kL1Bins of the device code)
 hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
-                       int ld_idx, void* ws, hipStream_t st);
+                       int ld_idx, void* ws, bool row_hist, hipStream_t st);
 
 // Round scores, selection and ragged expansion.
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,

@@ -238,7 +238,8 @@ template <typename T, int D, int NT, int RPT, int E>
 __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
                                                        int32_t* __restrict__ q_idx,
                                                        float* __restrict__ sq_out, int bcp,
-                                                       int nq_keep) {
+                                                       int nq_keep, u32x4* __restrict__ zero,
+                                                       int zero16) {
   constexpr int CH = D / 8;          // chunks per row (CH divides 64)
   constexpr int NRL = NT / CH;       // rows handled at once
   constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
@@ -251,6 +252,9 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   const int c = tid % CH, rl = tid / CH;
   const int bh = blockIdx.x;
   const T* qh = q + static_cast<size_t>(bh) * bcp * D;
+  // clears the buffer (zero16 16-byte words) that the scoring pass after this
+  // one accumulates into
+  for (int i = bh * NT + tid; i < zero16; i += static_cast<int>(gridDim.x) * NT) zero[i] = u32x4{0u, 0u, 0u, 0u};
 
   Raw8<T> rows[RPT > 0 ? RPT : 1];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -426,35 +430,35 @@ __global__ __launch_bounds__(64) void qgroup_kernel(const T* __restrict__ q,
 
 template <typename T, int D, int NT, int RPT>
 void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bcp, int nq_keep,
-                 hipStream_t st) {
+                 u32x4* zero, int zero16, hipStream_t st) {
   constexpr int NRL = NT / (D / 8);
   const dim3 grid(b * nq), block(NT);
   const T* qq = static_cast<const T*>(q);
   // up to 64 positions: one-wave sort; beyond: histogram selection
   if (bcp <= 64) {
     const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16);
   } else {
     const size_t part = std::max<size_t>(static_cast<size_t>(NRL) * D, hist_words(kQselBins) + 256 + bcp + 4);
     const size_t shm = sizeof(float) * (part + D + bcp);
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16);
   }
 }
 
 template <typename T, int D>
 hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, int nq, int nkv,
-               int bcp, int nq_keep, hipStream_t st) {
+               int bcp, int nq_keep, u32x4* zero, int zero16, hipStream_t st) {
   constexpr int CH = D / 8;
   if (bcp * CH <= 64) {
-    launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, st);   // decode-sized chunks
+    launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);   // decode-sized chunks
   } else if (bcp * CH <= 256) {
-    launch_head<T, D, 256, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, st);  // short chunks
+    launch_head<T, D, 256, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);  // short chunks
   } else {
     constexpr int NRL = 1024 / CH;
     const int rpt = (bcp + NRL - 1) / NRL;
-    if (rpt <= 4) launch_head<T, D, 1024, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
-    else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
-    else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, st);
+    if (rpt <= 4) launch_head<T, D, 1024, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
+    else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
+    else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
   }
   if (q_group)
     hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
@@ -465,15 +469,18 @@ hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, 
 }  // namespace
 
 hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group, int b,
-                       int nq, int nkv, int d, int bcp, int nq_keep, hipStream_t st) {
+                       int nq, int nkv, int d, int bcp, int nq_keep, int* zero, size_t zero_bytes,
+                       hipStream_t st) {
+  u32x4* z = reinterpret_cast<u32x4*>(zero);
+  const int z16 = zero ? static_cast<int>(zero_bytes / 16) : 0;
   if (bf16) {
-    if (d == 64) return run<uint16_t, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
-    if (d == 128) return run<uint16_t, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
-    if (d == 256) return run<uint16_t, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
+    if (d == 64) return run<uint16_t, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 128) return run<uint16_t, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 256) return run<uint16_t, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
   } else {
-    if (d == 64) return run<float, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
-    if (d == 128) return run<float, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
-    if (d == 256) return run<float, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, st);
+    if (d == 64) return run<float, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 128) return run<float, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 256) return run<float, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
   }
   return hipErrorInvalidValue;
 }

@@ -32,6 +32,7 @@ namespace qk {
 namespace {
 
 constexpr int kTopkThreads = 1024;
+static_assert(kL1Bins == kL1BinsHost, "one bin count for host and device");
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 4096;  // boundary-bin candidates kept in LDS
@@ -351,125 +352,158 @@ __global__ __launch_bounds__(256) void topk_all_kernel(int n, int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Split path for rows that are few or long: one row is spread over `slices`
-// workgroups of 1024 threads, each owning a tile of 1024 * IPT elements.
-//   pass 1 (topk_hist_kernel): each workgroup counting-sorts its tile by the
-//     level-1 bin of the order-preserving key (l1_bin below): it writes the
-//     tile's histogram, its exclusive prefix, and the tile's (key, position)
-//     pairs grouped by bin (workspace; nothing needs initialising);
-//   pass 2 (topk_split_kernel): each workgroup sums the row's histograms and
-//     finds the boundary bin B, reads bin B's pairs from every tile's groups
-//     into LDS, finds the k-th largest key among them (each ranked against
-//     the others when they are few, else radix levels over their key range),
-//     counts what earlier tiles contribute, and writes the positions picked
-//     in its own tile.
-// Workspace, for W = rows * slices workgroups: W histograms, W prefixes
-// (2048 ints each), then W tiles of (key, position) pairs.
+// Split path, for rows that are few or long: one row is spread over `slices`
+// workgroups of 1024 threads, each owning a tile of 1024 * IPT elements.  It
+// starts from the row's histogram over the level-1 bins (l1_bin): one per
+// row, filled by the scoring pass, or one per tile, written by
+// topk_tilehist_kernel just before (then summed).
+//   topk_cand_kernel, per tile: the boundary bin B of the row (where the k-th
+//     largest key lies) and the keys above it, from the histogram; writes the
+//     tile's keys of bin B with their positions (a few dozen at the cosine
+//     workloads' sizes), its count of bin-B keys and of keys above bin B;
+//   topk_pick_kernel, per tile: gathers the row's bin-B keys into LDS, finds
+//     tau, the need-th largest of them (the row's k-th largest key): few keys
+//     are ranked against the whole list, the work split over the block, more
+//     take radix levels over bin B's key range; then counts the keys > tau and
+//     == tau before its tile and writes its tile's picks.
+// A workgroup never reads more of the row than its own tile: on this chip one
+// CU pulls only some tens of GB/s from memory, so a tile per CU and a small
+// exchange through the workspace beat a full read of the row per workgroup.
+// Workspace, for W = rows * slices tiles (split_ws below): the W tile
+// histograms unless the scoring pass filled the row's, then per row (B, need,
+// count of bin B), per tile (bin-B count, count above bin B), and per tile
+// room for all of its keys as (key, position) pairs.  Nothing needs
+// initialising.
 // ---------------------------------------------------------------------------
-constexpr int kSplitCand = 6144;   // bin-B pairs kept in LDS
-constexpr int kCandPerThread = kSplitCand / kTopkThreads;
-constexpr int kRankDirect = 64;  // bin B ranked pair by pair up to this size
+constexpr int kSplitCand = 6144;  // bin-B keys kept in LDS
+constexpr int kMaxSlices = 1024;  // tiles per row (8M scores at 8 per thread)
+// bin-B slots per thread fetched before the counts are known: about four
+// times the count a tile of cosine scores holds at the workloads' sizes
+template <int IPT> constexpr int spec_per() { return IPT >= 8 ? 2 : 1; }
 
-// Level-1 bin of an order key (2048 bins), monotone in the key so that every
-// bin above the boundary bin is selected whole.  Each sign gets 1024 bins:
-// 64 per binade of |x| over [2^-8, 2^(1022/64 - 8)) (about 0.0039 to 250:
-// cosine scores and dot products of unit-scale vectors), one bin for the
-// smaller magnitudes next to zero and one for the larger ones (and NaN) at the
-// end.  The top bits of the key alone would spend most bins on exponents that
-// such scores never reach and put a tenth of a row into one bin.
-constexpr int kL1Shift = 17;         // key bits below a bin: 23 - 6 mantissa bits
-constexpr int kFineBase = 119 << 6;  // (exponent, top 6 mantissa bits) of 2^-8
-__device__ __forceinline__ int l1_bin(uint32_t key) {
-  const bool pos = key >= 0x80000000u;
-  const uint32_t mag = pos ? (key & 0x7fffffffu) : (0x7fffffffu - key);  // bits of |x|
-  const int v = static_cast<int>(mag >> kL1Shift) - kFineBase;
-  const int i = v < 0 ? 0 : min(v + 1, 1023);
-  return pos ? 1024 + i : 1023 - i;
-}
-// The keys of level-1 bin b: [*lo, *hi].
-__device__ __forceinline__ void l1_bin_range(int b, uint32_t* lo, uint32_t* hi) {
-  const bool pos = b >= 1024;
-  const int i = pos ? b - 1024 : 1023 - b;
-  const uint32_t mlo = i == 0 ? 0u : static_cast<uint32_t>(kFineBase + i - 1) << kL1Shift;
-  const uint32_t mhi =
-      i == 1023 ? 0x7fffffffu : (static_cast<uint32_t>(kFineBase + i) << kL1Shift) - 1u;
-  *lo = pos ? (0x80000000u | mlo) : (0x7fffffffu - mhi);
-  *hi = pos ? (0x80000000u | mhi) : (0x7fffffffu - mlo);
-}
+struct SplitWs {
+  int4* info;    // per row: (B, need, count of bin B in the row, 0)
+  int2* meta;    // per tile: (its bin-B count, its count above bin B)
+  uint2* slots;  // per tile: its bin-B keys and positions, tile-size slots
+};
 
+// Per-tile level-1 histograms (part[w * kL1Bins + b] for tile w of row
+// w / slices) when the scoring pass has not filled the rows'.
 template <int IPT, bool VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const float* __restrict__ scores,
-                                                                 int n, int ld_scores, int slices,
-                                                                 int* __restrict__ part) {
-  constexpr int kTile = kTopkThreads * IPT;
-  __shared__ int h[kBins];
-  __shared__ int wtot[kTopkWaves];
-  __shared__ uint4 stage[kTile / 2];  // the tile's pairs in bin order, two per entry
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int w = blockIdx.x, nwg = gridDim.x;
-  const int row = w / slices, sl = w - row * slices;
+__global__ __launch_bounds__(kTopkThreads) void topk_tilehist_kernel(const float* __restrict__ scores,
+                                                                     int n, int ld_scores, int slices,
+                                                                     int* __restrict__ part) {
+  __shared__ int h[kL1Bins];
+  static_assert(kL1Bins == 2 * kTopkThreads, "two bins per thread");
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x, row = w / slices, sl = w - row * slices;
   const float* s = scores + static_cast<size_t>(row) * ld_scores;
-  for (int i = tid; i < kBins; i += kTopkThreads) h[i] = 0;
+  for (int i = tid; i < kL1Bins; i += kTopkThreads) h[i] = 0;
   float x[IPT];
-  const uint32_t valid = load_tile<IPT, VEC>(s, sl * kTile, n, x);
-  uint32_t kx[IPT];
-#pragma unroll
-  for (int e = 0; e < IPT; ++e) kx[e] = fkey(x[e]);
+  const uint32_t valid = load_tile<IPT, VEC>(s, sl * kTopkThreads * IPT, n, x);
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < IPT; ++e)
-    if ((valid >> e) & 1u) atomicAdd(&h[l1_bin(kx[e])], 1);
+    if ((valid >> e) & 1u) atomicAdd(&h[l1_bin(fkey(x[e]))], 1);
   __syncthreads();
-  // exclusive prefix over the bins; thread t owns bins 2t and 2t + 1
-  const int c0 = h[2 * tid], c1 = h[2 * tid + 1];
-  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c0 + c1)));
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int off = 0;
-#pragma unroll
-  for (int v = 0; v < kTopkWaves; ++v) off += v < wave ? wtot[v] : 0;
-  const int ex = off + incl - c0 - c1;
-  h[2 * tid] = ex;  // now the bins' write cursors (each thread rewrites only its own bins)
-  h[2 * tid + 1] = ex + c0;
-  __syncthreads();
-  // The pairs are sorted into LDS and then written out contiguously: with
-  // scores spread over many bins, direct scattered 8-byte stores would each
-  // touch a line of their own.
-  uint2* lp = reinterpret_cast<uint2*>(stage);
-#pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    if ((valid >> e) & 1u) {
-      const int slot = atomicAdd(&h[l1_bin(kx[e])], 1);
-      if (slot < kTile)  // always: the slots of a bin end where the next bin's begin
-        lp[slot] = uint2{kx[e], static_cast<uint32_t>(tile_pos<IPT>(sl * kTile, e))};
-    }
-  }
-  __syncthreads();
-  uint4* pairs = reinterpret_cast<uint4*>(part + 2 * static_cast<size_t>(nwg) * kBins) +
-                 static_cast<size_t>(w) * (kTile / 2);
-  const int nvalid = min(kTile, n - sl * kTile);  // slots [0, nvalid) are filled
-  for (int i = tid; 2 * i < nvalid; i += kTopkThreads) pairs[i] = stage[i];
-  // the tile's histogram and prefix, stored after the last barrier (a store
-  // before a barrier holds the barrier until it completes)
-  *reinterpret_cast<int2*>(part + static_cast<size_t>(w) * kBins + 2 * tid) = int2{c0, c1};
-  *reinterpret_cast<int2*>(part + (static_cast<size_t>(nwg) + w) * kBins + 2 * tid) = int2{ex, ex + c0};
+  *reinterpret_cast<int2*>(part + static_cast<size_t>(w) * kL1Bins + 2 * tid) =
+      int2{h[2 * tid], h[2 * tid + 1]};
 }
 
-constexpr int kMaxSlices = 1024;
-
-struct SplitShared {
-  int hist2[kHistWords];      // radix levels over bin B's key range
-  alignas(16) uint32_t ckey[kSplitCand];
-  int cpos[kSplitCand];
-  int seg_start[kMaxSlices + 1];  // bin B's pairs of tile t: [seg_start[t], seg_start[t + 1])
-  int seg_off[kMaxSlices];        // ... found at this offset in tile t's sorted pairs
-  uint32_t wsum[kTopkWaves];
-  int red[2][kTopkWaves];
-  int bin[2], above[2], nb;
-  uint32_t tau;
-  int need;
+struct CandShared {
+  uint32_t wtot[kTopkWaves];
+  int red[kTopkWaves];
+  int bin, above, nb;
 };
 
+// hist: `hists` level-1 histograms per row (row r's at hist + r * hists *
+// kL1Bins) whose sum counts every score of the row once.
+template <int IPT, bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_cand_kernel(const float* __restrict__ scores,
+                                                                 int n, int k, int ld_scores,
+                                                                 int slices,
+                                                                 const int* __restrict__ hist,
+                                                                 int hists, SplitWs ws) {
+  __shared__ CandShared sh;
+  constexpr int kTile = kTopkThreads * IPT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int w = blockIdx.x, row = w / slices, sl = w - row * slices;
+  const float* s = scores + static_cast<size_t>(row) * ld_scores;
+  const int p0 = sl * kTile;  // first position of this workgroup's tile
+  const int* hrow = hist + static_cast<size_t>(row) * hists * kL1Bins;
+
+  // Its tile and the row's histograms are requested together (batches of 8
+  // histograms, addresses clamped so that a batch is branch-free); thread t
+  // sums bins 2t and 2t + 1.
+  float x[IPT];
+  const uint32_t valid = load_tile<IPT, VEC>(s, p0, n, x);
+  constexpr int kBatch = 8;
+  int total[2] = {0, 0};
+  if (hists == 1) {  // uniform: the row's histogram from the scoring pass
+    const int2 v = *reinterpret_cast<const int2*>(hrow + 2 * tid);
+    total[0] = v.x;
+    total[1] = v.y;
+  } else {
+    for (int h0 = 0; h0 < hists; h0 += kBatch) {
+      int2 v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = *reinterpret_cast<const int2*>(hrow + static_cast<size_t>(min(h0 + i, hists - 1)) * kL1Bins +
+                                              2 * tid);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        total[0] += h0 + i < hists ? v[i].x : 0;
+        total[1] += h0 + i < hists ? v[i].y : 0;
+      }
+    }
+  }
+  if (tid == 0) {  // defaults, overwritten below (ordered by the crossing's barriers)
+    sh.bin = 0;
+    sh.above = 0;
+    sh.nb = 0;
+  }
+  block_crossing(total[0], total[1], k, sh.red, &sh.bin, &sh.above, &sh.nb);
+  const int B = min(max(sh.bin, 0), kL1Bins - 1);
+  uint32_t lo, hi;
+  l1_bin_range(B, &lo, &hi);
+  const uint32_t span = hi - lo;  // key x is in bin B iff x - lo <= span (unsigned)
+
+  // the tile's bin-B keys, and its count above bin B
+  uint32_t cm = 0;
+  int above = 0;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const uint32_t kx = fkey(x[e]);
+    const bool v = (valid >> e) & 1u;
+    cm |= static_cast<uint32_t>(v && kx - lo <= span) << e;
+    above += (v && kx > hi) ? 1 : 0;
+  }
+  // packed (bin-B | above << 16) counts: a tile holds at most 8192 elements
+  const uint32_t mine = static_cast<uint32_t>(__popc(cm)) | (static_cast<uint32_t>(above) << 16);
+  const uint32_t incl = wave_incl_scan(mine);
+  if (lane == 63) sh.wtot[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int v = 0; v < kTopkWaves; ++v) {
+    const uint32_t t = sh.wtot[v];
+    tot += t;
+    before += v < wave ? t : 0u;
+  }
+  int at = static_cast<int>((before + incl - mine) & 0xffffu);
+  uint2* slot = ws.slots + static_cast<size_t>(w) * kTile;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    if ((cm >> e) & 1u) {
+      slot[at] = uint2{fkey(x[e]), static_cast<uint32_t>(tile_pos<IPT>(p0, e))};
+      ++at;
+    }
+  }
+  if (tid == 0) {
+    ws.meta[w] = int2{static_cast<int>(tot & 0xffffu), static_cast<int>(tot >> 16)};
+    if (sl == 0) ws.info[row] = int4{B, k - sh.above, sh.nb, 0};
+  }
+}
 
 // Sum over the block of (a, b); every thread gets the totals.
 __device__ __forceinline__ void block_sum2(int& a, int& b, int (*red)[kTopkWaves]) {
@@ -485,170 +519,159 @@ __device__ __forceinline__ void block_sum2(int& a, int& b, int (*red)[kTopkWaves
   __syncthreads();
 }
 
+struct PickShared {
+  int hist2[hist_words(1 << 11)];  // radix levels over bin B's key range
+  uint32_t ckey[kSplitCand];
+  int cpos[kSplitCand];
+  int seg[kMaxSlices];  // tile t's bin-B keys start at list position seg[t]
+  int cnt[kMaxSlices];  // ... and are cnt[t]
+  uint32_t wsum[kTopkWaves];
+  int red[2][kTopkWaves];
+  int bin, above;
+};
 
 template <int IPT, bool VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* __restrict__ scores,
-                                                                  int n, int k, int ld_scores,
-                                                                  int slices,
-                                                                  const int* __restrict__ part,
-                                                                  int32_t* __restrict__ idx,
-                                                                  int ld_idx) {
-  __shared__ SplitShared sh;
+__global__ __launch_bounds__(kTopkThreads) void topk_pick_kernel(const float* __restrict__ scores,
+                                                                 int n, int k, int ld_scores,
+                                                                 int slices, SplitWs ws,
+                                                                 int32_t* __restrict__ idx,
+                                                                 int ld_idx) {
+  __shared__ PickShared sh;
+  constexpr int kTile = kTopkThreads * IPT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = blockIdx.x / slices, sl = blockIdx.x - row * slices;
+  const int w = blockIdx.x, row = w / slices, sl = w - row * slices;
   const float* s = scores + static_cast<size_t>(row) * ld_scores;
   int32_t* out = idx + static_cast<size_t>(row) * ld_idx;
-  const int p0 = sl * kTopkThreads * IPT;  // first position of this workgroup's tile
-  const int* prow = part + static_cast<size_t>(row) * slices * kBins;
+  const int p0 = sl * kTile;
+  const uint2* srow = ws.slots + static_cast<size_t>(row) * slices * kTile;
 
-  // Its own tile and the row's tile histograms are requested together
-  // (batches of 8 tiles, addresses clamped so that a batch is branch-free).
-  // Thread t sums bins 2t and 2t + 1 over the tiles (all, and those before
-  // its own).
+  // One trip to memory: the tile, the row's (B, need), every tile's counts,
+  // and the first `cap` bin-B slots of every tile (before their counts are
+  // known; clamped addresses keep the loads branch-free).
+  // (B, need) through the vector path, issued first: as a scalar load (the
+  // address is uniform) it would be issued late and waited on alone
+  int row_v = row;
+  asm volatile("" : "+v"(row_v));
+  const int4 info = ws.info[row_v];
   float xo[IPT];
   const uint32_t vo = load_tile<IPT, VEC>(s, p0, n, xo);
-  static_assert(kBins == 2 * kTopkThreads, "two bins per thread");
-  constexpr int kBatch = 8;
-  int total[2] = {0, 0}, before[2] = {0, 0};
-  for (int s0 = 0; s0 < slices; s0 += kBatch) {
-    int2 v[kBatch];
+  const int2 m = ws.meta[static_cast<size_t>(row) * slices + min(tid, slices - 1)];
+  constexpr int kSpecPer = spec_per<IPT>();
+  const int cap = max(1, kSpecPer * kTopkThreads / slices);
+  uint2 sp[kSpecPer];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      v[i] = *reinterpret_cast<const int2*>(prow + static_cast<size_t>(min(s0 + i, slices - 1)) * kBins +
-                                            2 * tid);
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c0 = s0 + i < slices ? v[i].x : 0, c1 = s0 + i < slices ? v[i].y : 0;
-      total[0] += c0;
-      total[1] += c1;
-      before[0] += s0 + i < sl ? c0 : 0;
-      before[1] += s0 + i < sl ? c1 : 0;
-    }
+  for (int u = 0; u < kSpecPer; ++u) {
+    const int r = tid + kTopkThreads * u;
+    const int t = min(r / cap, slices - 1), j = min(r - (r / cap) * cap, kTile - 1);
+    sp[u] = srow[static_cast<size_t>(t) * kTile + j];
   }
 
-  // 1. boundary bin B of the row; bins above it in earlier tiles
-  block_crossing(total[0], total[1], k, sh.red[0], &sh.bin[0], &sh.above[0],
-                 &sh.nb);
-  const uint32_t B = static_cast<uint32_t>(min(max(sh.bin[0], 0), kBins - 1));
-  int need = k - sh.above[0];
-  const int nb = sh.nb;
-  int above_before = 0, unused = 0;
+  // list offsets of the tiles (a block scan of their counts), the count
+  // above bin B before this tile, and whether any tile holds more than `cap`
+  const int cx = tid < slices ? m.x : 0;
+  const int ax = tid < sl ? m.y : 0;
+  const int ox = cx > cap ? 1 : 0;
+  const uint32_t incl = wave_incl_scan(static_cast<uint32_t>(cx));
+  const int aw = static_cast<int>(lane63(wave_incl_scan(static_cast<uint32_t>(ax))));
+  const int ow = static_cast<int>(lane63(wave_incl_scan(static_cast<uint32_t>(ox))));
+  if (lane == 63) {
+    sh.red[0][wave] = static_cast<int>(incl);
+    sh.red[1][wave] = aw | (ow << 24);  // above_before < 2^24: rows hold at most 8M scores
+  }
+  __syncthreads();
+  int before = 0, nb = 0, above_before = 0, over = 0;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    above_before += static_cast<uint32_t>(2 * tid + u) > B ? before[u] : 0;
-
-  // 2. bin B's pairs of every tile -> LDS when they fit (else every visit
-  //    below reads them from the workspace)
+  for (int v = 0; v < kTopkWaves; ++v) {
+    const int c = sh.red[0][v];
+    nb += c;
+    before += v < wave ? c : 0;
+    above_before += sh.red[1][v] & 0xffffff;
+    over += sh.red[1][v] >> 24;
+  }
   if (tid < slices) {
-    const size_t t = static_cast<size_t>(row) * slices + tid;
-    sh.seg_start[tid + 1] = part[t * kBins + B];
-    sh.seg_off[tid] = part[(static_cast<size_t>(gridDim.x) + t) * kBins + B];
+    sh.seg[tid] = before + static_cast<int>(incl) - cx;
+    sh.cnt[tid] = cx;
   }
   __syncthreads();
-  if (wave == 0) {  // inclusive scan of the tiles' counts
-    int carry = 0;
-    for (int t0 = 0; t0 < slices; t0 += 64) {
-      const int c = static_cast<int>(
-          wave_incl_scan(static_cast<uint32_t>(t0 + lane < slices ? sh.seg_start[t0 + lane + 1] : 0)));
-      if (t0 + lane < slices) sh.seg_start[t0 + lane + 1] = carry + c;
-      carry += static_cast<int>(lane63(static_cast<uint32_t>(c)));
-    }
-    if (lane == 0) sh.seg_start[0] = 0;
-  }
-  __syncthreads();
-  const uint2* pairs = reinterpret_cast<const uint2*>(part + 2 * static_cast<size_t>(gridDim.x) * kBins);
-  constexpr int kTile = kTopkThreads * IPT;
-  auto fetch = [&](int i) {  // the i-th pair of bin B, 0 <= i < nb
-    int lo = 0, hi = slices - 1;  // the tile t with seg_start[t] <= i < seg_start[t + 1]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sh.seg_start[mid] <= i) lo = mid;
-      else hi = mid - 1;
-    }
-    const int at = min(max(sh.seg_off[lo] + (i - sh.seg_start[lo]), 0), kTile - 1);
-    return pairs[(static_cast<size_t>(row) * slices + lo) * kTile + at];
-  };
   const bool in_lds = nb <= kSplitCand;
+  const int ncand = in_lds ? nb : 0;
   if (in_lds) {
-    uint2 c[kCandPerThread];
 #pragma unroll
-    for (int r = 0; r < kCandPerThread; ++r) c[r] = fetch(min(tid + kTopkThreads * r, nb - 1));
-#pragma unroll
-    for (int r = 0; r < kCandPerThread; ++r) {
-      const int i = tid + kTopkThreads * r;
-      if (i < nb) {
-        sh.ckey[i] = c[r].x;
-        sh.cpos[i] = static_cast<int>(c[r].y);
+    for (int u = 0; u < kSpecPer; ++u) {
+      const int r = tid + kTopkThreads * u, t = r / cap, j = r - t * cap;
+      if (t < slices && j < sh.cnt[t]) {
+        const int at = sh.seg[t] + j;
+        sh.ckey[at] = sp[u].x;
+        sh.cpos[at] = static_cast<int>(sp[u].y);
+      }
+    }
+    if (over) {  // uniform: tiles with more than `cap` bin-B keys
+      for (int t = 0; t < slices; ++t) {
+        for (int j = cap + tid; j < sh.cnt[t]; j += kTopkThreads) {
+          const uint2 c = srow[static_cast<size_t>(t) * kTile + j];
+          sh.ckey[sh.seg[t] + j] = c.x;
+          sh.cpos[sh.seg[t] + j] = static_cast<int>(c.y);
+        }
       }
     }
   }
-  block_sum2(above_before, unused, sh.red);  // also orders the LDS list before its reads
-  auto visit = [&](auto f) {  // f(key, position) for every element of bin B
+  __syncthreads();
+
+  // f(key, position) for every key of bin B (from the list, or the slots)
+  auto visit = [&](auto f) __attribute__((always_inline)) {
     if (in_lds) {
-      for (int i = tid; i < nb; i += kTopkThreads) f(sh.ckey[i], sh.cpos[i]);
+      for (int i = tid; i < ncand; i += kTopkThreads) f(sh.ckey[i], sh.cpos[i]);
     } else {
-      for (int i = tid; i < nb; i += kTopkThreads) {
-        const uint2 c = fetch(i);
-        f(c.x, static_cast<int>(c.y));
+      for (int t = 0; t < slices; ++t) {
+        const int c = sh.cnt[t];
+        for (int j = tid; j < c; j += kTopkThreads) {
+          const uint2 p = srow[static_cast<size_t>(t) * kTile + j];
+          f(p.x, static_cast<int>(p.y));
+        }
       }
     }
   };
 
-  // 3. the k-th largest key tau of the row, the need-th largest of bin B
-  uint32_t tau;
-  if (in_lds && nb <= kRankDirect) {
-    // few: each candidate counts the greater and equal keys among the others
-    if (tid < nb) {
-      const uint32_t mine = sh.ckey[tid];
-      int gt = 0, eq = 0;
-      for (int c = 0; c < nb; ++c) {
-        const uint32_t o = sh.ckey[c];
-        gt += o > mine;
-        eq += o == mine;
+  // tau, and the copies of it still to take: radix levels over [base, base +
+  // width], the keys of bin B, until one key is left -- 9-bit digits over
+  // the LDS list (a small crossing per level; a bin's 2^17 keys take two
+  // levels), 11-bit digits when every visit re-reads the slots.  (Measured
+  // on a list of about 200 keys, the block-wide levels beat both a pairwise
+  // ranking and levels run by one wave.)
+  int need = info.y;
+  uint32_t base, hi;
+  l1_bin_range(min(max(info.x, 0), kL1Bins - 1), &base, &hi);
+  uint32_t width = hi - base;
+  auto levels = [&](auto dig) __attribute__((always_inline)) {
+    constexpr int DIG = decltype(dig)::value, NBIN = 1 << DIG;
+    while (width > 0) {  // uniform
+      const int shift = max(0, 32 - DIG - __clz(static_cast<int>(width)));  // width >> shift < NBIN
+      for (int i = tid; i < hist_words(NBIN); i += kTopkThreads) sh.hist2[i] = 0;
+      if (tid == 0) {  // (kept should no bin hold the crossing: the counts are exact)
+        sh.bin = 0;
+        sh.above = 0;
       }
-      if (gt < need && need <= gt + eq) {  // every holder of this key agrees
-        sh.tau = mine;
-        sh.need = need - gt;
-      }
+      __syncthreads();
+      visit([&](uint32_t kx, int) {
+        const uint32_t dx = kx - base;
+        if (kx >= base && dx <= width) atomicAdd(&sh.hist2[hpad(static_cast<int>(dx >> shift))], 1);
+      });
+      __syncthreads();
+      if (wave == 0) wave_crossing<NBIN / 64>(sh.hist2, need, &sh.bin, &sh.above);
+      __syncthreads();
+      need -= sh.above;
+      const uint32_t dg = static_cast<uint32_t>(min(max(sh.bin, 0), NBIN - 1)) << shift;
+      base += dg;
+      width = min(width - dg, (1u << shift) - 1u);
+      // bin / above are rewritten two barriers later, after every read
     }
-    __syncthreads();
-    tau = sh.tau;
-    need = sh.need;
-  } else {
-    // radix levels over [lo, lo + span], the keys of bin B, until one key is
-    // left: 9-bit digits over the LDS list (a small crossing per level; a fine
-    // bin's 2^17 keys take two levels), 11-bit digits when every visit
-    // re-reads the workspace
-    uint32_t lo, hi;
-    l1_bin_range(static_cast<int>(B), &lo, &hi);
-    uint32_t span = hi - lo;
-    auto levels = [&](auto dig) {
-      constexpr int DIG = decltype(dig)::value, NBIN = 1 << DIG;
-      while (span > 0) {  // uniform
-        const int shift = max(0, 32 - DIG - __clz(static_cast<int>(span)));  // span >> shift < NBIN
-        for (int i = tid; i < hist_words(NBIN); i += kTopkThreads) sh.hist2[i] = 0;
-        __syncthreads();
-        visit([&](uint32_t kx, int) {
-          const uint32_t dx = kx - lo;
-          if (kx >= lo && dx <= span) atomicAdd(&sh.hist2[hpad(static_cast<int>(dx >> shift))], 1);
-        });
-        __syncthreads();
-        if (wave == 0) wave_crossing<NBIN / 64>(sh.hist2, need, &sh.bin[1], &sh.above[1]);
-        __syncthreads();
-        need -= sh.above[1];
-        const uint32_t dg = static_cast<uint32_t>(min(max(sh.bin[1], 0), NBIN - 1)) << shift;
-        lo += dg;
-        span = min(span - dg, (1u << shift) - 1u);
-        // bin / above are rewritten two barriers later, after every read
-      }
-    };
-    if (in_lds) levels(std::integral_constant<int, 9>{});
-    else levels(std::integral_constant<int, 11>{});
-    tau = lo;
-  }
+  };
+  if (in_lds) levels(std::integral_constant<int, 9>{});
+  else levels(std::integral_constant<int, 11>{});
+  const uint32_t tau = base;
   // `need` copies of tau are taken (lowest positions first)
 
-  // 4. what earlier tiles contribute: greater keys and copies of tau
+  // what precedes this tile: greater keys and copies of tau
   int gt_before = 0, eq_before = 0;
   visit([&](uint32_t kx, int pos) {
     if (pos < p0) {
@@ -659,7 +682,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(const float* _
   block_sum2(gt_before, eq_before, sh.red);
   gt_before += above_before;
 
-  // 5. this tile's picks, in position order
+  // this tile's picks, in position order
   uint32_t gmask = 0, emask = 0;
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
@@ -682,31 +705,64 @@ bool split_shape(int rows, int n) {
   return n > 16 * kTopkThreads || (n > 4 * kTopkThreads && rows < 128);
 }
 
+// The split path's workspace for `rows` rows of n scores: the tile histograms
+// (unless the scoring pass fills one per row, row_hist; those then come
+// first, rows * kL1Bins ints), then the SplitWs arrays, each 16-byte aligned.
+struct SplitLayout {
+  size_t hist, info, meta, slots, total;
+};
+SplitLayout split_layout(int rows, int n, bool row_hist) {
+  auto up = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
+  const size_t tiles = static_cast<size_t>(rows) * split_slices(n);
+  SplitLayout l;
+  l.hist = 0;
+  l.info = up((row_hist ? static_cast<size_t>(rows) : tiles) * kL1Bins * sizeof(int));
+  l.meta = l.info + up(static_cast<size_t>(rows) * sizeof(int4));
+  l.slots = l.meta + up(tiles * sizeof(int2));
+  l.total = l.slots + tiles * kTopkThreads * split_items(n) * sizeof(uint2);
+  return l;
+}
+
 }  // namespace
 
-size_t topk_workspace_bytes(int rows, int n) {
+size_t topk_workspace_bytes(int rows, int n, bool row_hist) {
   if (rows <= 0 || n <= 0 || !split_shape(rows, n)) return 0;
-  const size_t tiles = static_cast<size_t>(rows) * split_slices(n);
-  return tiles * (2 * kBins * sizeof(int) + kTopkThreads * split_items(n) * sizeof(uint2));
+  return split_layout(rows, n, row_hist).total;
 }
 
 int topk_max_row() { return kMaxSlices * kTopkThreads * 8; }
 
+bool topk_uses_row_hist(int rows, int n, int k) { return k < n && split_shape(rows, n); }
+
+namespace {
+
+template <int IPT, bool VEC>
+void launch_split(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
+                  int ld_idx, char* ws, bool row_hist, hipStream_t st) {
+  const int slices = split_slices(n);
+  const dim3 grid(rows * slices), block(kTopkThreads);
+  const SplitLayout l = split_layout(rows, n, row_hist);
+  int* hist = reinterpret_cast<int*>(ws + l.hist);
+  SplitWs sw;
+  sw.info = reinterpret_cast<int4*>(ws + l.info);
+  sw.meta = reinterpret_cast<int2*>(ws + l.meta);
+  sw.slots = reinterpret_cast<uint2*>(ws + l.slots);
+  if (!row_hist)
+    hipLaunchKernelGGL((topk_tilehist_kernel<IPT, VEC>), grid, block, 0, st, scores, n, ld_scores, slices, hist);
+  hipLaunchKernelGGL((topk_cand_kernel<IPT, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices,
+                     hist, row_hist ? 1 : slices, sw);
+  hipLaunchKernelGGL((topk_pick_kernel<IPT, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices,
+                     sw, idx, ld_idx);
+}
+
 template <bool VEC>
 void launch_rows(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
-                 int ld_idx, void* ws, hipStream_t st) {
+                 int ld_idx, void* ws, bool row_hist, hipStream_t st) {
   const dim3 block(kTopkThreads);
   if (k < n && split_shape(rows, n)) {
-    const int slices = split_slices(n);
-    const dim3 grid(rows * slices);
-    int* part = static_cast<int*>(ws);
-    if (split_items(n) == 4) {
-      hipLaunchKernelGGL((topk_hist_kernel<4, VEC>), grid, block, 0, st, scores, n, ld_scores, slices, part);
-      hipLaunchKernelGGL((topk_split_kernel<4, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices, part, idx, ld_idx);
-    } else {
-      hipLaunchKernelGGL((topk_hist_kernel<8, VEC>), grid, block, 0, st, scores, n, ld_scores, slices, part);
-      hipLaunchKernelGGL((topk_split_kernel<8, VEC>), grid, block, 0, st, scores, n, k, ld_scores, slices, part, idx, ld_idx);
-    }
+    char* w = static_cast<char*>(ws);
+    if (split_items(n) == 4) launch_split<4, VEC>(rows, n, k, scores, ld_scores, idx, ld_idx, w, row_hist, st);
+    else launch_split<8, VEC>(rows, n, k, scores, ld_scores, idx, ld_idx, w, row_hist, st);
     return;
   }
   const dim3 grid(rows);
@@ -721,14 +777,16 @@ void launch_rows(int rows, int n, int k, const float* scores, int ld_scores, int
                        ld_idx);
 }
 
+}  // namespace
+
 hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_scores, int32_t* idx,
-                       int ld_idx, void* ws, hipStream_t st) {
+                       int ld_idx, void* ws, bool row_hist, hipStream_t st) {
   if (rows == 0 || n == 0) return hipSuccess;
   // 16-byte loads need aligned rows and whole groups of four
   const bool vec = (ld_scores % 4 == 0) && (n % 4 == 0) &&
                    (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
-  if (vec) launch_rows<true>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, st);
-  else launch_rows<false>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, st);
+  if (vec) launch_rows<true>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, row_hist, st);
+  else launch_rows<false>(rows, n, k, scores, ld_scores, idx, ld_idx, ws, row_hist, st);
   return hipGetLastError();
 }
 

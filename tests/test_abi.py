@@ -195,16 +195,32 @@ def test_workspace_sizes():
                                  "sparse_attn") == 0
     bad = qk.Shape(1, 7, 2, 128, 256, 32768, 33024, 32, 8192)
     assert qk.qk_workspace_bytes(bad, "sparse_attn") == 0
-    # top-k of a split row, per tile: a 2048-bin histogram and its prefix
-    # (ints), and the tile's (key, position) pairs
-    def tiles(t, size):
-        return t * (2 * 2048 * 4 + size * 8)
-    assert qk.topk_workspace_bytes(8, 32768) == tiles(8 * 8, 4096)
-    assert qk.topk_workspace_bytes(8, 131072) == tiles(8 * 16, 8192)
-    assert qk.topk_workspace_bytes(1, 300001) == tiles(37, 8192)
+    # top-k of a split row (tiles of 4096 scores up to 64K, else 8192): a
+    # 2048-bin histogram per tile (ints; one per row when the scoring pass
+    # fills them), (B, need, count) per row, two counts per tile, and a
+    # (key, position) slot for every score; each part 16-byte aligned
+    def split_ws(rows, n, row_hist=False):
+        tile = 4096 if n <= 65536 else 8192
+        t = rows * -(-n // tile)
+        up = lambda x: -(-x // 16) * 16
+        return (up((rows if row_hist else t) * 2048 * 4) + up(rows * 16) + up(t * 8)
+                + t * tile * 8)
+    assert qk.topk_workspace_bytes(8, 32768) == split_ws(8, 32768)
+    assert qk.topk_workspace_bytes(8, 131072) == split_ws(8, 131072)
+    assert qk.topk_workspace_bytes(1, 300001) == split_ws(1, 300001)
     assert qk.topk_workspace_bytes(512, 16384) == 0                    # one workgroup per row
-    assert qk.topk_workspace_bytes(512, 16388) == tiles(512 * 5, 4096)
+    assert qk.topk_workspace_bytes(512, 16388) == split_ws(512, 16388)
     assert qk.topk_workspace_bytes(8, 4096) == 0
+    # the whole selection: bf16 rows the top-k splits take one histogram per
+    # row, filled by the scoring pass; other shapes need what qk_topk needs
+    sel = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192)
+    assert qk.qk_workspace_bytes(sel, "select") == split_ws(8, 32768, row_hist=True)
+    sel32 = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192, dtype=qk.QK_F32)
+    assert qk.qk_workspace_bytes(sel32, "select") == split_ws(8, 32768)
+    dec = qk.Shape(64, 32, 8, 128, 1, 16384, 16385, 1, 2048)
+    assert qk.qk_workspace_bytes(dec, "select") == 0                   # one workgroup per row
+    assert qk.qk_workspace_bytes(qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 40000),
+                                 "select") == 0                        # every key kept
 
 
 def test_noalloc_scratch_covers_every_plan():

@@ -56,6 +56,9 @@ def test_full_size(gpu, name):
             gpu_sel_len=npi(pipe.sel_len[sl]) if rounds else None, what=f"{name} b{bi}")
         err = staged_attention(qn, kn, vn, spec.t_past, sets, pipe.out[sl], spec.dtype,
                                gpu_lse=pipe.lse[sl], what=f"{name} b{bi}")
+        if not rounds:  # integer stage, exact: the top-BSA of the GPU's own scores
+            want = oracle.select_keys(np64(pipe.s_agg[sl]), s.bsa)
+            assert np.array_equal(npi(pipe.idx[sl])[..., :want.shape[-1]], want)
         print(f"[full-size] {name} b{bi}: {st}, attention err {err:.2e} (every row and head)",
               flush=True)
 
@@ -98,3 +101,29 @@ def test_full_size_scoring_variants(gpu, name, mode, e4m3):
                            what=f"{name} {mode}")
     print(f"[full-size variant] {name} {mode} e4m3={e4m3} b{bi}: {st}, attention {err:.2e}",
           flush=True)
+
+
+@pytest.mark.parametrize("name", ["llama3b_32k", "long_128k", "long_128k_d256", "decode_64x16k"])
+def test_full_size_select_equals_separate_calls(gpu, name):
+    """At full size, the one-call selection the benchmark times (qk_select: the
+    scoring pass fills the histogram its top-k starts from) writes what
+    qk_qsel, qk_kvscore_grouped and qk_topk write one by one, bit for bit,
+    twice in a row on one workspace; and its key sets are the exact top-BSA of
+    its scores."""
+    qk = gpu
+    dev = torch.device("cuda:0")
+    spec = W.spec(name)
+    print(f"[full-size select] {name}", flush=True)
+    case = W.make_case(spec, FULL[name], device=dev)
+    s = qk.shape_of(spec)
+    a = qk.Pipeline(s, device=dev, fused_select=True)
+    b = qk.Pipeline(s, device=dev, fused_select=False)
+    b.select(case["q"], case["k"])
+    for _ in range(2):
+        a.idx.fill_(-1)
+        a.select(case["q"], case["k"])
+        torch.cuda.synchronize()
+        for x, y in ((a.q_idx, b.q_idx), (a.sq, b.sq), (a.s_agg, b.s_agg), (a.idx, b.idx)):
+            assert torch.equal(x, y)
+    want = oracle.select_keys(np64(a.s_agg), s.bsa)
+    assert np.array_equal(npi(a.idx)[..., :want.shape[-1]], want)

@@ -313,6 +313,46 @@ def test_pipeline_variants_end_to_end(gpu, name, mode, e4m3):
     print(f"[variant] {name} {mode} e4m3={e4m3}: {st}, attention {err:.2e}")
 
 
+SELECT_CASES = ["llama_ragged", "d256_small", "decode_small", "tiny_f32", "g1_all_keys",
+                "d64_nq40"]
+
+
+@pytest.mark.parametrize("name", SELECT_CASES)
+@pytest.mark.parametrize("mode,e4m3", [("cosine", False)] + VARIANTS)
+def test_select_equals_separate_calls(gpu, name, mode, e4m3):
+    """qk_select writes what qk_qsel, qk_kvscore_variant and qk_topk write one
+    by one, bit for bit: also where its scoring pass fills the histogram the
+    top-k starts from (bf16 rows spread over several workgroups:
+    llama_ragged, d256_small), from a workspace full of stale bytes, and on a
+    second call that reuses the workspace."""
+    qk = gpu
+    spec, case, ref, g = _case(name)
+    if e4m3 and spec.dtype != "bf16":
+        pytest.skip("8-bit keys are scored with bf16 queries only")
+    s = _shape(spec, qk)
+    a = qk.Pipeline(s, device=_dev(), score_mode=mode, k_e4m3=e4m3, fused_select=True)
+    b = qk.Pipeline(s, device=_dev(), score_mode=mode, k_e4m3=e4m3, fused_select=False)
+    assert a.fused_select and not b.fused_select
+    for p in (a, b):
+        if e4m3:
+            p.store_keys_e4m3(g["k"])
+    if a.select_ws is not None:
+        a.select_ws.fill_(0x7f)
+    b.select(g["q"], g["k"])
+    for _ in range(2):
+        for t in (a.q_idx, a.sq, a.s_agg, a.idx):
+            t.fill_(-3)
+        a.select(g["q"], g["k"])
+        torch.cuda.synchronize()
+        assert torch.equal(a.q_idx, b.q_idx)
+        assert torch.equal(a.sq, b.sq)
+        assert torch.equal(a.s_agg, b.s_agg)
+        assert torch.equal(a.idx, b.idx)
+    # and the selection is the exact top-BSA of the scores it was taken on
+    want = oracle.select_keys(np64(a.s_agg), s.bsa)
+    assert np.array_equal(npi(a.idx)[..., :want.shape[-1]], want)
+
+
 def test_kvscore_grouped_unsorted_positions(gpu):
     """The group means pair slot n of every head whatever the positions are:
     kept positions given in an arbitrary (unsorted, repeated) order score like
@@ -443,6 +483,9 @@ def test_pipeline_end_to_end(gpu, name):
                            what=name)
     if spec.dtype == "f32":
         assert st["swaps"] == 0
+    # integer stage, exact: the key sets are the top-BSA of the GPU's own scores
+    want = oracle.select_keys(np64(pipe.s_agg), spec.bsa)
+    assert np.array_equal(npi(pipe.idx)[..., :want.shape[-1]], want)
     print(f"[e2e] {name}: {st}, attention {err:.2e}")
 
 
