@@ -338,9 +338,10 @@ def main():
     def step(i):
         c = inputs[i % copies]
         if e4m3:
+            # the chunk's own key rows become E4M3 codes too (the append):
+            # inside qk_select's scoring pass
             pipe.k8 = c["k8"]
-            pipe.store_keys_e4m3(c["k"], spec.t_past, spec.bcp)
-        pipe.select(c["q"], c["k"], c["round_off"])
+        pipe.select(c["q"], c["k"], c["round_off"], append_e4m3=e4m3)
         pipe.attend(c["q"], c["k"], c["v"])
 
     for i in range(args.warmup):
@@ -376,7 +377,9 @@ def main():
         elif name == "select_one_call":
             # qk_select: query selection, scoring (with the histogram the
             # top-k starts from) and top-k in one call, as the timed step runs
-            pipe.select(c["q"], c["k"])
+            if e4m3:
+                pipe.k8 = c["k8"]
+            pipe.select(c["q"], c["k"], append_e4m3=e4m3)
         elif name == "select":
             if rounds:
                 qk.qk_round_select(shape, pipe.s_agg, spec.n_rounds, c["round_off"],

@@ -224,10 +224,17 @@ qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores,
  * starts from, which saves the top-k its own counting pass.  Scratch:
  * qk_workspace_bytes(QK_OP_SELECT) bytes (ws, 16-byte aligned; NULL allowed
  * when that is 0).  Needs T >= 1 and bsa >= 1 (else QK_ERR_SHAPE); other
- * limits and errors as the three calls. */
+ * limits and errors as the three calls.
+ * k_new: NULL, or -- with QK_KEYS_E4M3 -- the dtype cache (b,nkv,kv_cap,d),
+ * 16-byte aligned, whose chunk rows [T, T + bcp) the scoring pass also stores
+ * as E4M3 codes into k (the 8-bit copy), byte for byte what
+ * qk_keys_to_e4m3(s, k_new, T, bcp, k) writes: the rows this chunk appends,
+ * for the chunks after it (this call scores rows [0, T) only).  Non-NULL with
+ * QK_KEYS_DTYPE is QK_ERR_UNSUPPORTED. */
 qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key_format,
-                    int32_t mode, int32_t* q_idx, float* sq, float* s_agg, int32_t* idx,
-                    int32_t ld_idx, void* ws, size_t ws_bytes, qk_stream_t stream);
+                    int32_t mode, const void* k_new, int32_t* q_idx, float* sq, float* s_agg,
+                    int32_t* idx, int32_t ld_idx, void* ws, size_t ws_bytes,
+                    qk_stream_t stream);
 
 /* Round-granular selection (Round Attention press release, sections 01-02).
  * round_off: (n_rounds + 1) int32, off[0] = 0, strictly increasing,

@@ -104,7 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_kvscore_variant": ([F, P, P, P, I, I, P, P], I),
         "qk_keys_to_e4m3": ([F, P, I, I, P, P], I),
         "qk_topk": ([I, I, I, P, I, P, I, P, SZ, P], I),
-        "qk_select": ([F, P, P, I, I, P, P, P, P, I, P, SZ, P], I),
+        "qk_select": ([F, P, P, I, I, P, P, P, P, P, I, P, SZ, P], I),
         "qk_round_select": ([F, P, I, P, I, I, P, I, P, P, P, P], I),
         "qk_gather": ([F, P, P, P, I, P, P, P, P], I),
         "qk_sparse_attn": ([F, P, P, P, I, P, P, P, P, P, P, SZ, P], I),
@@ -208,15 +208,17 @@ def qk_topk(rows, n, k, scores, ld_scores, idx, ld_idx, ws=None, ws_bytes=0, str
 
 
 def qk_select(shape, q, k, key_format, mode, q_idx, sq, s_agg, idx, ld_idx, ws=None, ws_bytes=0,
-              stream=None):
+              stream=None, k_new=None):
     """qk_qsel + qk_kvscore_variant + qk_topk in one call.  ws=None: a
-    workspace of the required size is allocated for this call."""
+    workspace of the required size is allocated for this call.  k_new (8-bit
+    keys only): the dtype cache whose chunk rows the scoring pass also stores
+    as E4M3 codes into k."""
     mode = SCORE_MODES[mode] if isinstance(mode, str) else int(mode)
     if ws is None:
         ws, ws_bytes = _ws(shape, "select", q.device)
     _check("qk_select", load_library().qk_select(
-        _sh(shape), _ptr(q), _ptr(k), int(key_format), mode, _ptr(q_idx), _ptr(sq), _ptr(s_agg),
-        _ptr(idx), ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
+        _sh(shape), _ptr(q), _ptr(k), int(key_format), mode, _ptr(k_new), _ptr(q_idx), _ptr(sq),
+        _ptr(s_agg), _ptr(idx), ld_idx, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def qk_round_select(shape, s_agg, n_rounds, round_off, top_r, keep_latest, idx, ld_idx,
@@ -367,14 +369,20 @@ class Pipeline:
         else:
             qk_kvscore(s, self.q_group, k, self.s_agg)
 
-    def select(self, q, k, round_off=None):
+    def select(self, q, k, round_off=None, append_e4m3=False):
+        """append_e4m3 (8-bit keys): also store the chunk's own key rows
+        [t_past, t_past + bcp) of k as E4M3 codes in k8, for later chunks (in
+        the scoring pass of qk_select, else by qk_keys_to_e4m3 first)."""
         s = self.shape
+        append_e4m3 = append_e4m3 and self.k_e4m3
         if self.fused_select:
             qk_select(s, q, self.k8 if self.k_e4m3 else k,
                       QK_KEYS_E4M3 if self.k_e4m3 else QK_KEYS_DTYPE, self.score_mode, self.q_idx,
                       self.sq, self.s_agg, self.idx, self.ld_idx, self.select_ws,
-                      self.select_ws_bytes)
+                      self.select_ws_bytes, k_new=k if append_e4m3 else None)
             return
+        if append_e4m3:
+            self.store_keys_e4m3(k, s.t_past, s.bcp)
         self.score(q, k)
         if self.n_rounds:
             qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds,

@@ -60,7 +60,8 @@ qk_status check_ws(const qk_shape* s, int32_t op, const void* ws, size_t ws_byte
 qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
                          const int32_t* q_idx, const void* k, float* s_agg, qk_stream_t stream,
                          bool k_e4m3 = false, bool dot = false, bool check_only = false,
-                         int* hist = nullptr) {
+                         int* hist = nullptr, const void* q_kept = nullptr,
+                         const void* conv_src = nullptr) {
   qk_status st = check_shape(s);
   if (st != QK_OK) return st;
   if (!k || !s_agg) return QK_ERR_NULL;
@@ -92,6 +93,9 @@ qk_status kvscore_common(const qk_shape* s, const float* q_group, const void* q,
   c.k_e4m3 = k_e4m3;
   c.dot = dot;
   c.hist = hist;
+  c.q_kept = q_kept;
+  c.conv_src = conv_src;
+  c.conv_dst = conv_src ? static_cast<uint8_t*>(const_cast<void*>(k)) : nullptr;
   if (check_only) return QK_OK;
   return hip_status(qk::launch_kvscore(c, hs(stream)));
 }
@@ -112,9 +116,19 @@ qk_status qsel_check(const qk_shape* s, const void* q, const int32_t* q_idx, con
 inline bool select_row_hist(const qk_shape* s) {
   return is_bf16(s) && qk::topk_uses_row_hist(s->b * s->nkv, s->t_past, s->bsa);
 }
-size_t select_ws_bytes(const qk_shape* s) {
+// qk_select's workspace: the top-k's (starting with the rows' histograms when
+// the scoring pass fills them), then -- bf16 -- the kept query rows in rank
+// order, (b, nq, NQ, d), which the query pass writes and the scoring pass
+// reads instead of looking the positions up.
+size_t select_topk_bytes(const qk_shape* s) {
   if (s->bsa >= s->t_past) return 0;  // every key kept: nothing to count
   return qk::topk_workspace_bytes(s->b * s->nkv, s->t_past, select_row_hist(s));
+}
+size_t select_kept_offset(const qk_shape* s) { return (select_topk_bytes(s) + 255) & ~static_cast<size_t>(255); }
+size_t select_ws_bytes(const qk_shape* s) {
+  if (!is_bf16(s)) return select_topk_bytes(s);
+  return select_kept_offset(s) +
+         static_cast<size_t>(s->b) * s->nq * s->nq_keep * s->d * sizeof(uint16_t);
 }
 // Bytes at the start of the qk_select workspace that the scoring pass
 // accumulates into (cleared by the query pass before it).
@@ -161,7 +175,7 @@ qk_status qk_qsel(const qk_shape* s, const void* q, int32_t* q_idx, float* sq, f
   const qk_status st = qsel_check(s, q, q_idx, sq, q_group);
   if (st != QK_OK) return st;
   return hip_status(qk::launch_qsel(is_bf16(s), q, q_idx, sq, q_group, s->b, s->nq, s->nkv, s->d,
-                                    s->bcp, s->nq_keep, nullptr, 0, hs(stream)));
+                                    s->bcp, s->nq_keep, nullptr, 0, nullptr, hs(stream)));
 }
 
 qk_status qk_kvscore(const qk_shape* s, const float* q_group, const void* k, float* s_agg,
@@ -218,14 +232,17 @@ qk_status qk_topk(int32_t rows, int32_t n, int32_t k, const float* scores, int32
 }
 
 qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key_format,
-                    int32_t mode, int32_t* q_idx, float* sq, float* s_agg, int32_t* idx,
-                    int32_t ld_idx, void* ws, size_t ws_bytes, qk_stream_t stream) {
+                    int32_t mode, const void* k_new, int32_t* q_idx, float* sq, float* s_agg,
+                    int32_t* idx, int32_t ld_idx, void* ws, size_t ws_bytes,
+                    qk_stream_t stream) {
   qk_status st = qsel_check(s, q, q_idx, sq, nullptr);
   if (st != QK_OK) return st;
   if ((key_format != QK_KEYS_DTYPE && key_format != QK_KEYS_E4M3) ||
       (mode != QK_SCORE_COSINE && mode != QK_SCORE_DOT))
     return QK_ERR_UNSUPPORTED;
   const bool e4m3 = key_format == QK_KEYS_E4M3, dot = mode == QK_SCORE_DOT;
+  if (k_new && !e4m3) return QK_ERR_UNSUPPORTED;
+  if (k_new && !aligned16(k_new)) return QK_ERR_ALIGN;
   st = kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, e4m3, dot, true);
   if (st != QK_OK) return st;
   if (s->t_past < 1 || s->bsa < 1) return QK_ERR_SHAPE;
@@ -238,11 +255,13 @@ qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key
   if (st != QK_OK) return st;
   const bool row_hist = select_row_hist(s);
   int* hist = row_hist ? static_cast<int*>(ws) : nullptr;
+  void* q_kept = is_bf16(s) ? static_cast<char*>(ws) + select_kept_offset(s) : nullptr;
   hipError_t e = qk::launch_qsel(is_bf16(s), q, q_idx, sq, nullptr, s->b, s->nq, s->nkv, s->d,
                                  s->bcp, s->nq_keep, hist, row_hist ? select_hist_bytes(s) : 0,
-                                 hs(stream));
+                                 q_kept, hs(stream));
   if (e != hipSuccess) return QK_ERR_HIP;
-  st = kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, e4m3, dot, false, hist);
+  st = kvscore_common(s, nullptr, q, q_idx, k, s_agg, stream, e4m3, dot, false, hist, q_kept,
+                      k_new);
   if (st != QK_OK) return st;
   return hip_status(qk::launch_topk(rows, n, s->bsa, s_agg, n, idx, ld_idx, ws, row_hist,
                                     hs(stream)));

@@ -6,36 +6,13 @@
 // pass reads 8-bit keys: it is bound by the bytes of K it streams, and E4M3
 // halves them.  Attention keeps the bf16 rows.
 //
-// Encoding (OCP 8-bit floating point, E4M3): sign, 4 exponent bits (bias 7),
-// 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6.  Each value
-// takes the nearest code, ties to the even code; magnitudes above 448 (the
-// largest finite code) saturate to 448; the sign bit is copied, so values that
-// round to zero keep it.  Callers convert the rows a chunk appends, once.
+// Encoding: e4m3_code (device header).  Callers convert the rows a chunk
+// appends, once (qk_select can do it inside its scoring pass instead).
 #include "qk_device.h"
 #include "qk_internal.h"
 
 namespace qk {
 namespace {
-
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.0f);
-  uint32_t code;
-  if (a < 0x1p-6f) {
-    // below the smallest normal the codes are the multiples of 2^-9: adding
-    // 2^14 (whose fp32 spacing is 2^-9) rounds to the nearest one, ties to
-    // even; 2^-6 itself comes out as 8, the smallest normal code
-    const float r = __fsub_rn(__fadd_rn(a, 0x1p14f), 0x1p14f);
-    code = static_cast<uint32_t>(r * 512.0f);
-  } else {
-    // keep 3 of the 23 mantissa bits, rounding to nearest even (a carry moves
-    // into the exponent), then rebias the exponent from 127 to 7
-    const uint32_t b = __float_as_uint(a);
-    const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  return sign | code;
-}
 
 // One thread per 16 consecutive elements of a row (d is a multiple of 16).
 template <typename T>
@@ -70,12 +47,7 @@ __global__ __launch_bounds__(256) void keys_e4m3_kernel(const T* __restrict__ k,
       for (int e = 0; e < 4; ++e) x[4 * h + e] = w[e];
     }
   }
-  u32x4 out;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    out[w] = e4m3_code(x[4 * w]) | (e4m3_code(x[4 * w + 1]) << 8) | (e4m3_code(x[4 * w + 2]) << 16) |
-             (e4m3_code(x[4 * w + 3]) << 24);
-  st16(k8 + off, out);
+  st16(k8 + off, e4m3x16(x));
 }
 
 }  // namespace

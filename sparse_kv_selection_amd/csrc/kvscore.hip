@@ -39,9 +39,13 @@ struct ScoreArgs {
   const float* q_group;    // (b, nkv, nq_keep, d) fp32, or nullptr: formed from q / q_idx
   const uint16_t* q;       // (b, nq, bcp, d) the chunk's queries
   const int32_t* q_idx;    // (b, nq, nq_keep) kept positions
+  const uint16_t* q_kept;  // (b, nq, nq_keep, d) the kept rows by rank, or nullptr
   const void* k;           // (b, nkv, kv_cap, d) bf16, or E4M3 bytes
   float* s_agg;
   int* hist;               // (b * nkv, kL1Bins) zeroed level-1 histograms, or nullptr
+  const uint16_t* conv_src;  // bf16 cache whose chunk rows are stored as E4M3 codes, or nullptr
+  uint8_t* conv_dst;         // ... into this 8-bit copy (same element positions)
+  int conv_total;            // (b, KV head, chunk row, 16 elements) units to convert
   int nkv, group, bcp, t_past, kv_cap, nq_keep;
   int blocks_per_bj, wgs_per_bj;
 };
@@ -72,6 +76,22 @@ struct GroupBuild {
   // are unconditional, so the wait before their use counts exactly them)
   __device__ __forceinline__ void issue(const ScoreArgs& a, int bj, int g0) {
     const int b = bj / a.nkv, j = bj - b * a.nkv;
+    if (a.q_kept) {  // uniform: the kept rows gathered by the query pass, one trip
+      const uint16_t* kr = a.q_kept + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.nq_keep * D +
+                           8 * (threadIdx.x % CH);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = min((static_cast<int>(threadIdx.x) + 64 * kScoreWaves * u) / CH, a.nq_keep - 1);
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+          const int g = min(g0 + gg, a.group - 1);
+          x[u][gg] = ld16(kr + (static_cast<size_t>(g) * a.nq_keep + n) * D);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     const int32_t* qi = a.q_idx + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.nq_keep;
     const uint16_t* qb = a.q + (static_cast<size_t>(b) * a.nkv + j) * a.group * a.bcp * D;
     const int c = threadIdx.x % CH;
@@ -225,6 +245,44 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
   GBuild gb;
   if constexpr (GROUPED) gb.issue(a, bj, 0);  // kept positions, then their rows
 
+  // The chunk's own key rows stored as E4M3 codes (qk_select with 8-bit keys:
+  // the rows this chunk appends, scored by later passes).  The grid's
+  // workgroups split the (b, KV head, row, 16 elements) units; up to d <= 128
+  // a thread's first unit is requested with the kept rows, before any key,
+  // and stored once the query build has waited for them; the rest (and every
+  // unit at d = 256, whose registers are full) at the end.
+  const int conv_total = a.conv_dst ? a.conv_total : 0;  // uniform
+  const int conv_per = conv_total ? (conv_total + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x) : 0;
+  const int conv_lo = static_cast<int>(blockIdx.x) * conv_per;
+  const int conv_hi = min(conv_lo + conv_per, conv_total);
+  auto conv_off = [&](int u) {  // element offset of unit u in the cache
+    constexpr int UPR = D / 16;
+    const int c16 = u % UPR, rr = u / UPR;
+    const int r = rr % a.bcp, bjc = rr / a.bcp;
+    return (static_cast<size_t>(bjc) * a.kv_cap + a.t_past + r) * D + 16 * c16;
+  };
+  auto conv_store = [&](size_t off, const u32x4* w) {
+    float x[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * h + 2 * e] = bf16lo(w[h][e]);
+        x[8 * h + 2 * e + 1] = bf16hi(w[h][e]);
+      }
+    st16(a.conv_dst + off, e4m3x16(x));
+  };
+  constexpr bool kConvEarly = D <= 128;
+  u32x4 cw[2] = {u32x4{}, u32x4{}};
+  size_t coff = 0;
+  if constexpr (kConvEarly) {
+    if (conv_total) {  // uniform; clamped, so every thread loads
+      coff = conv_off(min(conv_lo + static_cast<int>(threadIdx.x), conv_total - 1));
+      cw[0] = ld16(a.conv_src + coff);
+      cw[1] = ld16(a.conv_src + coff + 8);
+    }
+  }
+
   u32x4 buf[STAGES][NL];
   auto load_block = [&](int blk, u32x4* dst) {
     const int row = min(blk * kBlock + col, a.kv_cap - 1);
@@ -236,11 +294,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
   // are unconditional (a wave with fewer blocks re-reads its first one, or a
   // clamped row): behind a branch, the wait before the kept rows' first use
   // would have to assume that no key load is in flight and wait for all.
-  // Grouped: one block before the kept rows are used, the rest of the ring
-  // after.  Every key request in flight on the chip delays the kept rows
-  // (they queue behind the key lines in the memory pipeline), and the rows
-  // gate every wave's first product; one block per wave measured best.
-  constexpr int kEarly = GROUPED ? 1 : STAGES - 1;
+  // Grouped, shallow ring (few blocks per wave, short rows): one block before
+  // the kept rows are used, the rest of the ring after.  Every key request in
+  // flight on the chip delays the kept rows (they queue behind the key lines
+  // in the memory pipeline), and the rows gate every wave's first product;
+  // one block per wave measured best there.  With the deep ring (long rows)
+  // the whole ring goes out first: the wait for the rows is then covered
+  // (measured 5 % faster at 128K keys, 7 % slower at 32K).
+  constexpr int kEarly = (GROUPED && STAGES <= 3) ? 1 : STAGES - 1;
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
   __builtin_amdgcn_sched_barrier(0);
@@ -250,10 +311,13 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
     __shared__ __align__(16) uint16_t s_hi[GBuild::ROWS * GBuild::LD];
     __shared__ __align__(16) uint16_t s_lo[GBuild::ROWS * GBuild::LD];
     gb.template build<DOT>(a, bj, s_hi, s_lo);
+    if constexpr (kConvEarly)
+      if (conv_total && conv_lo + static_cast<int>(threadIdx.x) < conv_hi) conv_store(coff, cw);
 #pragma unroll
     for (int i = kEarly; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
     lds_barrier();
-    if (nblk == 0 && !with_hist) return;  // (with the histogram, every wave meets its barrier)
+    // (with the histogram or a conversion, every wave goes on to the end)
+    if (nblk == 0 && !with_hist && !conv_total) return;
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
       int row = mb * 32 + col;
@@ -267,7 +331,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
     }
   } else {
     if (with_hist) lds_barrier();  // the cleared histogram before any count
-    if (nblk == 0 && !with_hist) return;
+    if (nblk == 0 && !with_hist && !conv_total) return;
     const float* qg = a.q_group + static_cast<size_t>(bj) * a.nq_keep * D;
 #pragma unroll
     for (int mb = 0; mb < NQB; ++mb) {
@@ -362,6 +426,12 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
       score_block(block_of(m), buf[i]);
     }
   }
+  for (int u = conv_lo + (kConvEarly ? 64 * kScoreWaves : 0) + static_cast<int>(threadIdx.x); u < conv_hi;
+       u += 64 * kScoreWaves) {
+    const size_t off = conv_off(u);
+    const u32x4 w[2] = {ld16(a.conv_src + off), ld16(a.conv_src + off + 8)};
+    conv_store(off, w);
+  }
   if (with_hist) {
     lds_barrier();
     int* gh = a.hist + static_cast<size_t>(bj) * kL1Bins;
@@ -453,9 +523,13 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   a.q_group = c.q_group;
   a.q = static_cast<const uint16_t*>(c.q);
   a.q_idx = c.q_idx;
+  a.q_kept = static_cast<const uint16_t*>(c.q_kept);
   a.k = c.k;
   a.s_agg = c.s_agg;
   a.hist = c.hist;
+  a.conv_src = static_cast<const uint16_t*>(c.conv_src);
+  a.conv_dst = c.conv_dst;
+  a.conv_total = c.conv_src ? c.b * c.nkv * c.bcp * (c.d / 16) : 0;
   a.nkv = c.nkv;
   a.group = c.nq / c.nkv;
   a.bcp = c.bcp;

@@ -202,6 +202,41 @@ __device__ __forceinline__ void l1_bin_range(int b, uint32_t* lo, uint32_t* hi) 
   *hi = pos ? (0x80000000u | mhi) : (0x7fffffffu - mlo);
 }
 
+// OCP 8-bit floating point, E4M3: sign, 4 exponent bits (bias 7), 3 mantissa
+// bits; exponent field 0 holds the subnormals m/8 * 2^-6.  Each value takes
+// the nearest code, ties to the even code; magnitudes above 448 (the largest
+// finite code) saturate to 448; the sign bit is copied, so values that round
+// to zero keep it.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    // below the smallest normal the codes are the multiples of 2^-9: adding
+    // 2^14 (whose fp32 spacing is 2^-9) rounds to the nearest one, ties to
+    // even; 2^-6 itself comes out as 8, the smallest normal code
+    const float r = __fsub_rn(__fadd_rn(a, 0x1p14f), 0x1p14f);
+    code = static_cast<uint32_t>(r * 512.0f);
+  } else {
+    // keep 3 of the 23 mantissa bits, rounding to nearest even (a carry moves
+    // into the exponent), then rebias the exponent from 127 to 7
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// 16 values as E4M3 codes, value e in byte e.
+__device__ __forceinline__ u32x4 e4m3x16(const float* x) {
+  u32x4 out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    out[w] = e4m3_code(x[4 * w]) | (e4m3_code(x[4 * w + 1]) << 8) | (e4m3_code(x[4 * w + 2]) << 16) |
+             (e4m3_code(x[4 * w + 3]) << 24);
+  return out;
+}
+
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) {
   return group_reduce<64>(v, [](float a, float b) { return fmaxf(a, b); });

@@ -8,10 +8,12 @@ namespace qk {
 
 // Query sub-selection + group aggregation.  zero: nullptr, or zero_bytes (a
 // multiple of 16) of 16-byte aligned memory that the kernel also clears (the
-// histograms of the scoring pass that follows).
+// histograms of the scoring pass that follows).  q_kept: nullptr, or
+// (b, nq, nq_keep, d) in q's dtype, 16-byte aligned, to which the kept rows
+// are copied in rank order.
 hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group,
                        int b, int nq, int nkv, int d, int bcp, int nq_keep, int* zero,
-                       size_t zero_bytes, hipStream_t st);
+                       size_t zero_bytes, void* q_kept, hipStream_t st);
 
 // Key scoring pass.  q_group == nullptr: the group queries are formed from
 // (q, q_idx) inside the scoring kernel.
@@ -28,6 +30,13 @@ struct ScoreCall {
   // bf16 only: nullptr, or (b * nkv, kL1Bins) int32, zeroed, to which the pass
   // adds every row's histogram of its scores over the level-1 bins
   int* hist = nullptr;
+  // bf16 grouped only: nullptr, or (b, nq, nq_keep, d) the kept rows by rank,
+  // as the query pass gathers them (q_idx is then not read)
+  const void* q_kept = nullptr;
+  // bf16 grouped only: nullptr, or the bf16 cache whose chunk rows [t_past,
+  // t_past + bcp) the pass also stores as E4M3 codes into conv_dst
+  const void* conv_src = nullptr;
+  uint8_t* conv_dst = nullptr;
 };
 hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
 

@@ -47,6 +47,7 @@ template <> struct Raw8<uint16_t> {
                                            __builtin_shufflevector(v, v, 6, 7), n2, false);
   }
   __device__ __forceinline__ void zero() { w = u32x4{}; }
+  __device__ __forceinline__ void store(uint16_t* p) const { st16(p, w); }
 };
 template <> struct Raw8<float> {
   f32x4 a, b;
@@ -65,6 +66,10 @@ template <> struct Raw8<float> {
     return n2;
   }
   __device__ __forceinline__ void zero() { a = f32x4{}; b = f32x4{}; }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
+  }
 };
 
 __device__ __forceinline__ uint32_t okey(float x) { return order_key(x); }
@@ -131,7 +136,8 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
 
 // Wave 0 of the block: top-NQ positions of sq[0..bcp) by decreasing score.
 template <int E>
-__device__ __forceinline__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* out) {
+__device__ __forceinline__ void top_positions(const float* sq, int bcp, int nq_keep, int32_t* out,
+                                              int* kmap) {
   const int lane = threadIdx.x & 63;
   uint64_t v[E];
 #pragma unroll
@@ -143,7 +149,12 @@ __device__ __forceinline__ void top_positions(const float* sq, int bcp, int nq_k
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int p = lane * E + e;
-    if (p < nq_keep) out[p] = static_cast<int32_t>(~static_cast<uint32_t>(v[e]));
+    if (p < nq_keep) {
+      const int32_t i = static_cast<int32_t>(~static_cast<uint32_t>(v[e]));
+      out[p] = i;
+      kmap[i] = p;
+      kmap[bcp + p] = i;
+    }
   }
 }
 
@@ -171,7 +182,8 @@ __device__ __forceinline__ void select_clear(int* scratch, int bcp) {
 }
 template <int NT>
 __device__ __forceinline__ void top_positions_select(const float* sq, int* scratch, int bcp, int nq_keep,
-                                                     int32_t* out, const float (*red)[NT / 64]) {
+                                                     int32_t* out, int* kmap,
+                                                     const float (*red)[NT / 64]) {
   constexpr int kB = kQselBins, kWaves = NT / 64, TPP = 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* hist = scratch;
@@ -223,8 +235,15 @@ __device__ __forceinline__ void top_positions_select(const float* sq, int* scrat
     for (int j = part; j < n; j += TPP) r += key(list[j]) > ki;
     r = group_sum<TPP>(r);
     if (part == 0 && n > 0) {
-      if (a) out[r] = i;
-      else if (r < need) out[na + r] = i;
+      if (a) {
+        out[r] = i;
+        kmap[i] = r;
+        kmap[bcp + r] = i;
+      } else if (r < need) {
+        out[na + r] = i;
+        kmap[i] = na + r;
+        kmap[bcp + na + r] = i;
+      }
     }
   }
 }
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
                                                        int32_t* __restrict__ q_idx,
                                                        float* __restrict__ sq_out, int bcp,
                                                        int nq_keep, u32x4* __restrict__ zero,
-                                                       int zero16) {
+                                                       int zero16, T* __restrict__ q_kept) {
   constexpr int CH = D / 8;          // chunks per row (CH divides 64)
   constexpr int NRL = NT / CH;       // rows handled at once
   constexpr int S = NT / D > 0 ? NT / D : 1;  // lanes per column in the column sum
@@ -248,6 +267,8 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
                                      // NRL rows), then the selection scratch
   float* mq = part + (E > 0 ? NRL * D : max(NRL * D, hist_words(kQselBins) + 256 + bcp + 4));  // [D]
   float* sq = mq + D;                // [bcp]
+  // [bcp] rank of a kept position, else -1; then [NQ] the kept positions by rank
+  int* kmap = reinterpret_cast<int*>(sq + bcp);
   const int tid = threadIdx.x;
   const int c = tid % CH, rl = tid / CH;
   const int bh = blockIdx.x;
@@ -255,6 +276,7 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   // clears the buffer (zero16 16-byte words) that the scoring pass after this
   // one accumulates into
   for (int i = bh * NT + tid; i < zero16; i += static_cast<int>(gridDim.x) * NT) zero[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < bcp; i += NT) kmap[i] = -1;  // (ordered by the barriers below)
 
   Raw8<T> rows[RPT > 0 ? RPT : 1];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -371,9 +393,30 @@ __global__ __launch_bounds__(NT) void qsel_head_kernel(const T* __restrict__ q,
   __syncthreads();
   int32_t* out = q_idx + static_cast<size_t>(bh) * nq_keep;
   if constexpr (E > 0) {
-    if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out);
+    if (tid < 64) top_positions<E>(sq, bcp, nq_keep, out, kmap);
   } else {
-    top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out, red);
+    top_positions_select<NT>(sq, reinterpret_cast<int*>(part), bcp, nq_keep, out, kmap, red);
+  }
+  // The kept rows themselves, by rank (q_kept: (b, nq, NQ, d), the chunk's
+  // dtype), for a scoring pass that then needs no kept position to find them:
+  // rows held in registers go out from there, others are read again.
+  if (q_kept) {  // uniform
+    __syncthreads();
+    T* kh = q_kept + static_cast<size_t>(bh) * nq_keep * D + 8 * c;
+    if constexpr (RPT > 0) {
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        const int i = u * NRL + rl;
+        const int r = i < bcp ? kmap[i] : -1;
+        if (r >= 0) rows[u].store(kh + static_cast<size_t>(r) * D);
+      }
+    } else {
+      for (int r = rl; r < nq_keep; r += NRL) {
+        Raw8<T> x;
+        x.load(qh + static_cast<size_t>(kmap[bcp + r]) * D + 8 * c);
+        x.store(kh + static_cast<size_t>(r) * D);
+      }
+    }
   }
   // SQ goes out last, coalesced from LDS (unchanged since the barrier above):
   // a global store issued before a barrier would hold that barrier until the
@@ -430,35 +473,35 @@ __global__ __launch_bounds__(64) void qgroup_kernel(const T* __restrict__ q,
 
 template <typename T, int D, int NT, int RPT>
 void launch_head(const void* q, int32_t* q_idx, float* sq, int b, int nq, int bcp, int nq_keep,
-                 u32x4* zero, int zero16, hipStream_t st) {
+                 u32x4* zero, int zero16, void* q_kept, hipStream_t st) {
   constexpr int NRL = NT / (D / 8);
   const dim3 grid(b * nq), block(NT);
   const T* qq = static_cast<const T*>(q);
   // up to 64 positions: one-wave sort; beyond: histogram selection
   if (bcp <= 64) {
-    const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + bcp);
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16);
+    const size_t shm = sizeof(float) * (static_cast<size_t>(NRL) * D + D + 2 * bcp + 256);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 1>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16, static_cast<T*>(q_kept));
   } else {
     const size_t part = std::max<size_t>(static_cast<size_t>(NRL) * D, hist_words(kQselBins) + 256 + bcp + 4);
-    const size_t shm = sizeof(float) * (part + D + bcp);
-    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16);
+    const size_t shm = sizeof(float) * (part + D + 2 * bcp + 256);
+    hipLaunchKernelGGL((qsel_head_kernel<T, D, NT, RPT, 0>), grid, block, shm, st, qq, q_idx, sq, bcp, nq_keep, zero, zero16, static_cast<T*>(q_kept));
   }
 }
 
 template <typename T, int D>
 hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, int nq, int nkv,
-               int bcp, int nq_keep, u32x4* zero, int zero16, hipStream_t st) {
+               int bcp, int nq_keep, u32x4* zero, int zero16, void* q_kept, hipStream_t st) {
   constexpr int CH = D / 8;
   if (bcp * CH <= 64) {
-    launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);   // decode-sized chunks
+    launch_head<T, D, 64, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, q_kept, st);   // decode-sized chunks
   } else if (bcp * CH <= 256) {
-    launch_head<T, D, 256, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);  // short chunks
+    launch_head<T, D, 256, 1>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, q_kept, st);  // short chunks
   } else {
     constexpr int NRL = 1024 / CH;
     const int rpt = (bcp + NRL - 1) / NRL;
-    if (rpt <= 4) launch_head<T, D, 1024, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
-    else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
-    else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, st);
+    if (rpt <= 4) launch_head<T, D, 1024, 4>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, q_kept, st);
+    else if (rpt <= 8) launch_head<T, D, 1024, 8>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, q_kept, st);
+    else launch_head<T, D, 1024, 0>(q, q_idx, sq, b, nq, bcp, nq_keep, zero, zero16, q_kept, st);
   }
   if (q_group)
     hipLaunchKernelGGL((qgroup_kernel<T, D>), dim3(b * nkv * nq_keep), dim3(64), 0, st,
@@ -470,17 +513,17 @@ hipError_t run(const void* q, int32_t* q_idx, float* sq, float* q_group, int b, 
 
 hipError_t launch_qsel(bool bf16, const void* q, int32_t* q_idx, float* sq, float* q_group, int b,
                        int nq, int nkv, int d, int bcp, int nq_keep, int* zero, size_t zero_bytes,
-                       hipStream_t st) {
+                       void* q_kept, hipStream_t st) {
   u32x4* z = reinterpret_cast<u32x4*>(zero);
   const int z16 = zero ? static_cast<int>(zero_bytes / 16) : 0;
   if (bf16) {
-    if (d == 64) return run<uint16_t, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
-    if (d == 128) return run<uint16_t, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
-    if (d == 256) return run<uint16_t, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 64) return run<uint16_t, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
+    if (d == 128) return run<uint16_t, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
+    if (d == 256) return run<uint16_t, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
   } else {
-    if (d == 64) return run<float, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
-    if (d == 128) return run<float, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
-    if (d == 256) return run<float, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, st);
+    if (d == 64) return run<float, 64>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
+    if (d == 128) return run<float, 128>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
+    if (d == 256) return run<float, 256>(q, q_idx, sq, q_group, b, nq, nkv, bcp, nq_keep, z, z16, q_kept, st);
   }
   return hipErrorInvalidValue;
 }

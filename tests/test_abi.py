@@ -211,16 +211,19 @@ def test_workspace_sizes():
     assert qk.topk_workspace_bytes(512, 16384) == 0                    # one workgroup per row
     assert qk.topk_workspace_bytes(512, 16388) == split_ws(512, 16388)
     assert qk.topk_workspace_bytes(8, 4096) == 0
-    # the whole selection: bf16 rows the top-k splits take one histogram per
-    # row, filled by the scoring pass; other shapes need what qk_topk needs
+    # the whole selection: what the top-k needs (bf16 rows it splits take one
+    # histogram per row, filled by the scoring pass), then for bf16 the kept
+    # query rows (b, nq, NQ, d) at a 256-byte boundary
+    up256 = lambda x: -(-x // 256) * 256
     sel = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192)
-    assert qk.qk_workspace_bytes(sel, "select") == split_ws(8, 32768, row_hist=True)
+    assert qk.qk_workspace_bytes(sel, "select") == (up256(split_ws(8, 32768, row_hist=True))
+                                                    + 24 * 32 * 128 * 2)
     sel32 = qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 8192, dtype=qk.QK_F32)
     assert qk.qk_workspace_bytes(sel32, "select") == split_ws(8, 32768)
     dec = qk.Shape(64, 32, 8, 128, 1, 16384, 16385, 1, 2048)
-    assert qk.qk_workspace_bytes(dec, "select") == 0                   # one workgroup per row
+    assert qk.qk_workspace_bytes(dec, "select") == 64 * 32 * 1 * 128 * 2   # one workgroup per row
     assert qk.qk_workspace_bytes(qk.Shape(1, 24, 8, 128, 256, 32768, 33024, 32, 40000),
-                                 "select") == 0                        # every key kept
+                                 "select") == 24 * 32 * 128 * 2        # every key kept
 
 
 def test_noalloc_scratch_covers_every_plan():

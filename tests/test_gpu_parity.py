@@ -324,7 +324,9 @@ def test_select_equals_separate_calls(gpu, name, mode, e4m3):
     by one, bit for bit: also where its scoring pass fills the histogram the
     top-k starts from (bf16 rows spread over several workgroups:
     llama_ragged, d256_small), from a workspace full of stale bytes, and on a
-    second call that reuses the workspace."""
+    second call that reuses the workspace.  With 8-bit keys the scoring pass
+    also stores the chunk's own key rows, byte for byte what qk_keys_to_e4m3
+    writes."""
     qk = gpu
     spec, case, ref, g = _case(name)
     if e4m3 and spec.dtype != "bf16":
@@ -342,12 +344,16 @@ def test_select_equals_separate_calls(gpu, name, mode, e4m3):
     for _ in range(2):
         for t in (a.q_idx, a.sq, a.s_agg, a.idx):
             t.fill_(-3)
-        a.select(g["q"], g["k"])
+        if e4m3:  # the chunk's own rows of the 8-bit copy come from the scoring pass
+            a.k8[:, :, s.t_past:s.t_past + s.bcp] = 0x55
+        a.select(g["q"], g["k"], append_e4m3=e4m3)
         torch.cuda.synchronize()
         assert torch.equal(a.q_idx, b.q_idx)
         assert torch.equal(a.sq, b.sq)
         assert torch.equal(a.s_agg, b.s_agg)
         assert torch.equal(a.idx, b.idx)
+        if e4m3:
+            assert torch.equal(a.k8, b.k8)
     # and the selection is the exact top-BSA of the scores it was taken on
     want = oracle.select_keys(np64(a.s_agg), s.bsa)
     assert np.array_equal(npi(a.idx)[..., :want.shape[-1]], want)
