@@ -40,10 +40,16 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # followed by the shared device header): once either changes, the figure no
 # longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 69909709),
-    ("llama3b_32k", "attention"): ("attention.hip", "fd00fc37fa3ea8bb", 71477043),
-    ("long_128k", "kvscore"): ("kvscore.hip", "af5ac5ac267f2062", 277107098),
-    ("long_128k", "attention"): ("attention.hip", "fd00fc37fa3ea8bb", 122580582),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "54204ba83534e21a", 70637677),
+    ("llama3b_32k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 72448384),
+    ("long_128k", "kvscore"): ("kvscore.hip", "54204ba83534e21a", 278019776),
+    ("long_128k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 123568048),
+    ("decode_64x16k", "kvscore"): ("kvscore.hip", "54204ba83534e21a", 2181906290),
+    ("decode_64x16k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 542617114),
+    ("rounds_64k", "kvscore"): ("kvscore.hip", "54204ba83534e21a", 138849584),
+    ("rounds_64k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 95261616),
+    ("long_128k_d256", "kvscore"): ("kvscore.hip", "54204ba83534e21a", 550303890),
+    ("long_128k_d256", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 173053504),
 }
 
 
@@ -418,7 +424,10 @@ def main():
                   "traffic": None if variant else measured_traffic(spec.name, "kvscore"),
                   "algorithmic_bytes": work["score_bytes"],
                   "ms": round(stage_ms["kvscore"], 5)}
-    attn_kernels = ("qk_sparse_attn_indexed (attn_bf16_kernel"
+    # the attention plan's choice: the eight-wave ping-pong kernel at d = 128
+    # when a KV head has more than 128 query rows
+    pp = spec.d == 128 and (spec.nq // spec.nkv) * spec.bcp > 128
+    attn_kernels = ("qk_sparse_attn_indexed (" + ("attn_pp_kernel" if pp else "attn_bf16_kernel")
                     + (" + attn_combine_kernel)" if pipe_splits(shape) > 1 else ")"))
     if spec.bcp == 1:
         attn_gbs = work["attn_bytes"] / (stage_ms["attention"] * 1e-3) / 1e9
