@@ -247,6 +247,20 @@ def select_rounds(s_round, top_r: int, keep_latest: bool = True):
     return chosen
 
 
+def select_rounds_shared(s_round, top_r: int, keep_latest: bool = True):
+    """One round choice for all KV heads of a sequence (a variant of the
+    per-head choice above, so that a caller that keeps rounds off the GPU
+    brings in top_r + 1 rounds rather than the union of every head's).
+    Reading: the shared score of round r is the largest of the sequence's KV
+    heads' round scores (a round matters if it matters to some head); the
+    chosen rounds are picked by that score exactly as select_rounds picks them
+    per head, and every head gets the same list."""
+    s_round = f64(s_round)
+    shared = s_round.max(axis=1, keepdims=True)  # (b, 1, R)
+    one = select_rounds(shared, top_r, keep_latest)
+    return [[row[0].copy() for _ in range(s_round.shape[1])] for row in one]
+
+
 def round_key_sets(chosen, round_off):
     """Expand chosen round ids to the ascending past positions they cover."""
     off = np.asarray(round_off, dtype=np.int64)

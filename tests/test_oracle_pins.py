@@ -429,6 +429,29 @@ def test_rounds_bruteforce_and_limits():
         assert sets1[0][j].tolist() == want
 
 
+def test_rounds_shared_by_the_heads():
+    """The head-shared round choice: a hand-worked case (the shared score is
+    the per-round maximum over the heads: (0.45, 0.5, 0.45) over the first
+    three rounds, so round 1 joins the latest; per head the choices differ),
+    one KV head reducing to the per-head choice, and on random scores the
+    brute-force ranking of the per-round maxima."""
+    sr = np.array([[[0.1, 0.5, 0.45, 0.0], [0.45, 0.1, 0.4, 0.9]]])
+    assert [c.tolist() for c in Q.select_rounds(sr, 1)[0]] == [[1, 3], [0, 3]]
+    assert [c.tolist() for c in Q.select_rounds_shared(sr, 1)[0]] == [[1, 3], [1, 3]]
+    assert [c.tolist() for c in Q.select_rounds_shared(sr, 2)[0]] == [[0, 1, 3], [0, 1, 3]]
+    rng = np.random.default_rng(41)
+    one = rng.standard_normal((2, 1, 9))
+    for keep in (True, False):
+        a, b = Q.select_rounds(one, 3, keep), Q.select_rounds_shared(one, 3, keep)
+        assert all(np.array_equal(a[i][0], b[i][0]) for i in range(2))
+    x = np.round(rng.standard_normal((3, 4, 10)), 1)  # ties between rounds
+    got = Q.select_rounds_shared(x, 4)
+    for bi in range(3):
+        m = [max(x[bi, j, r] for j in range(4)) for r in range(10)]
+        want = sorted(_brute_rank(m[:9])[:4] + [9])
+        assert all(g.tolist() == want for g in got[bi])
+
+
 # ----------------------------------------------------------------------------
 # 7. the pins catch planted mistakes
 # ----------------------------------------------------------------------------
@@ -662,6 +685,8 @@ def _pins_pass(mod):
         op2, _ = mod.prompt_chunks(qp, kp, vp, 4, 2, bsa=3, n_decode=2)
         for t in (7, 8):
             ok &= np.array_equal(op2[:, :, t:t + 1], mod.pipeline(qp[:, :, t:t + 1], kp, vp, t, 1, 3)["o"])
+        srs = np.array([[[0.1, 0.5, 0.45, 0.0], [0.45, 0.1, 0.4, 0.9]]])
+        ok &= [c.tolist() for c in mod.select_rounds_shared(srs, 1)[0]] == [[1, 3], [1, 3]]
         mags = mod.e4m3_decode(np.arange(0x7F))
         lo = np.arange(0x7E)
         ok &= np.array_equal(mod.e4m3_encode((mags[:-1] + mags[1:]) / 2),
@@ -693,6 +718,10 @@ MUTATIONS = {
                               "r = pipeline(q[:, :, t:t + n], k, v, max(t - 1, 0), keep, bsa, score=score, k_e4m3=k_e4m3)"),
     "decode keeps the chunk rule": ("n = min(bcp, prompt - t) if t < prompt else 1",
                                     "n = min(bcp, total - t)"),
+    "shared rounds by mean": ("shared = s_round.max(axis=1, keepdims=True)",
+                              "shared = s_round.mean(axis=1, keepdims=True)"),
+    "shared rounds by min": ("shared = s_round.max(axis=1, keepdims=True)",
+                             "shared = s_round.min(axis=1, keepdims=True)"),
     "dot sums heads": ("return sel.reshape(b, nkv, G, sel.shape[2], d).mean(axis=2)",
                        "return sel.reshape(b, nkv, G, sel.shape[2], d).sum(axis=2)"),
 }
