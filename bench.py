@@ -206,7 +206,9 @@ def bench_offload(spec, args, dev):
         sys.exit("--offload-layers needs a round workload (rounds_64k)")
     L, w, T, n = args.offload_layers, args.watershed, spec.t_past, spec.bcp
     off = W.round_offsets(T, spec.n_rounds, args.seed)
-    stack = driver.RoundOffloadStack(L, w, off, spec.b, spec.nkv, spec.d, n, device=dev)
+    shared = args.shared_rounds
+    stack = driver.RoundOffloadStack(L, w, off, spec.b, spec.nkv, spec.d, n, device=dev,
+                                     shared_rounds=shared)
     caches, qs, krows, vrows = [], [], [], []
     for layer in range(L):
         case = W.make_case(spec, args.seed + 7919 * layer, device=dev)
@@ -226,7 +228,8 @@ def bench_offload(spec, args, dev):
         for c in caches:
             c.length = T
         return driver.layer_stack_step(qs, caches, krows, vrows, spec.nq_keep, plan, w,
-                                       round_off=off_dev, top_rounds=spec.top_rounds)
+                                       round_off=off_dev, top_rounds=spec.top_rounds,
+                                       shared_rounds=shared)
 
     def offload():
         return stack.step(qs, krows, vrows, spec.nq_keep, spec.top_rounds, plan)
@@ -256,13 +259,17 @@ def bench_offload(spec, args, dev):
         "ms_per_step": round(ms_off, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
         "config": {"workload": f"{spec.name}: {_describe(spec)}", "layers": L, "watershed": w,
+                   "round_choice": "shared by the KV heads" if shared else "per KV head",
                    "rounds_copied": len(stack.last_rounds)},
         "resident_stack_ms": round(ms_res, 4),
         "h2d_bytes_per_chunk": h2d,
         "h2d_copy_ms": round(copy_ms, 4),
         "h2d_gbps": round(h2d / (copy_ms * 1e-3) / 1e9, 2) if copy_ms > 0 else None,
-        "gpu_kv_bytes": stack.device_kv_bytes(), "resident_kv_bytes": stack.resident_kv_bytes(),
-        "gpu_kv_saved_frac": round(1 - stack.device_kv_bytes() / stack.resident_kv_bytes(), 4),
+        # GPU KV: the lower layers' caches plus two staging caches holding the
+        # chosen rounds (and the chunk) of the last step
+        "staged_past_positions": stack.last_staged,
+        "gpu_kv_bytes": stack.staged_kv_bytes(), "resident_kv_bytes": stack.resident_kv_bytes(),
+        "gpu_kv_saved_frac": round(1 - stack.staged_kv_bytes() / stack.resident_kv_bytes(), 4),
         "outputs_equal_resident": same,
         "timing": "wall clock over whole steps (the step waits on the host for the watershed's "
                   "selection before it schedules the copies)",
@@ -292,6 +299,8 @@ def main():
                     help="round workloads: a stack of this many layers whose layers above the "
                          "watershed keep their KV per round in pinned host memory")
     ap.add_argument("--watershed", type=int, default=1)
+    ap.add_argument("--shared-rounds", action="store_true",
+                    help="with --offload-layers: one round choice for all KV heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()

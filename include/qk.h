@@ -236,19 +236,31 @@ qk_status qk_select(const qk_shape* s, const void* q, const void* k, int32_t key
                     int32_t* idx, int32_t ld_idx, void* ws, size_t ws_bytes,
                     qk_stream_t stream);
 
+/* Flags of qk_round_select's keep_latest argument (0 and 1 keep their
+ * meaning: nothing, and the latest round kept). */
+#define QK_ROUNDS_KEEP_LATEST 1 /* the latest round is always kept                    */
+#define QK_ROUNDS_SHARED 2      /* one choice for all KV heads of a sequence (see below) */
+
 /* Round-granular selection (Round Attention press release, sections 01-02).
  * round_off: (n_rounds + 1) int32, off[0] = 0, strictly increasing,
  * off[n_rounds] = t_past.  For each (b, KV head):
  *   s_round[r] = max over off[r] <= t < off[r+1] of s_agg[b,j,t]
  *   chosen     = {n_rounds-1} and the top_r best of the other rounds when
- *                keep_latest != 0 (else the top_r best of all); ties: lower id
+ *                keep_latest has QK_ROUNDS_KEEP_LATEST (else the top_r best of
+ *                all); ties: lower id
  *   idx[b,j,0..sel_len) = every position of the chosen rounds, ascending
+ * With QK_ROUNDS_SHARED the rounds are ranked by max over the sequence's KV
+ * heads j' of s_round[b,j',r], and every head of the sequence gets the same
+ * rounds: a caller that keeps rounds off the GPU then brings in top_r (+ 1)
+ * rounds rather than the union of every head's choice.  s_round keeps each
+ * head's own round scores.
  * idx: (b,nkv,ld_idx) int32 with ld_idx >= the largest possible selection
  * (t_past is always enough); sel_len: (b,nkv) int32; s_round: (b,nkv,n_rounds)
- * f32 or NULL; chosen: (b,nkv,n_rounds) uint8 or NULL, 1 where round r is one
- * of head (b,j)'s chosen rounds, else 0 (what a caller that keeps rounds off
- * the GPU needs to know to bring them in).  1 <= top_r, top_r +
- * (keep_latest != 0) <= n_rounds <= 4096. */
+ * f32, or NULL without QK_ROUNDS_SHARED (else QK_ERR_NULL); chosen:
+ * (b,nkv,n_rounds) uint8 or NULL, 1 where round r is one of head (b,j)'s
+ * chosen rounds, else 0 (what a caller that keeps rounds off the GPU needs to
+ * know to bring them in).  1 <= top_r, top_r + (1 with QK_ROUNDS_KEEP_LATEST)
+ * <= n_rounds <= 4096; other flag bits: QK_ERR_UNSUPPORTED. */
 qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_rounds,
                           const int32_t* round_off, int32_t top_r,
                           int32_t keep_latest, int32_t* idx, int32_t ld_idx,

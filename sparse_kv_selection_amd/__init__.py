@@ -27,6 +27,7 @@ OPS = {"qsel": 0, "kvscore": 1, "topk": 2, "round_select": 3, "gather": 4,
        "sparse_attn": 5, "dense_attn": 6, "select": 7}
 QK_SCORE_COSINE, QK_SCORE_DOT = 0, 1    # qk_score_mode
 QK_KEYS_DTYPE, QK_KEYS_E4M3 = 0, 1      # qk_key_format
+QK_ROUNDS_KEEP_LATEST, QK_ROUNDS_SHARED = 1, 2   # qk_round_select flags
 SCORE_MODES = {"cosine": QK_SCORE_COSINE, "dot": QK_SCORE_DOT}
 EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel",
             "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
@@ -298,6 +299,9 @@ class Pipeline:
     caller fills with ``store_keys_e4m3`` as rows are appended to the cache
     (attention still reads the bf16 keys).  Both variants need ``fused_group``.
 
+    ``shared_rounds`` (round selection): one round choice for all KV heads of
+    a sequence (QK_ROUNDS_SHARED).
+
     ``fused_select``: top-BSA selection (no rounds) with ``fused_group`` goes
     through qk_select, one call for qsel, scoring and top-k; otherwise the
     three calls are made one by one (same results, bit for bit).
@@ -306,7 +310,7 @@ class Pipeline:
     def __init__(self, shape: Shape, device="cuda", n_rounds: int = 0, top_rounds: int = 0,
                  keep_latest: bool = True, fused_gather: bool = True, with_lse: bool = True,
                  fused_group: bool = True, score_mode: str = "cosine", k_e4m3: bool = False,
-                 fused_select: bool = True):
+                 fused_select: bool = True, shared_rounds: bool = False):
         s = self.shape = shape
         if score_mode not in SCORE_MODES:
             raise ValueError("score_mode is 'cosine' or 'dot'")
@@ -315,6 +319,7 @@ class Pipeline:
         self.score_mode, self.k_e4m3 = score_mode, k_e4m3
         self.device = torch.device(device)
         self.n_rounds, self.top_rounds, self.keep_latest = n_rounds, top_rounds, keep_latest
+        self.shared_rounds = shared_rounds
         self.fused_gather, self.fused_group = fused_gather, fused_group
         self.fused_select = (fused_select and fused_group and not n_rounds and s.t_past >= 1
                              and s.bsa >= 1)
@@ -385,9 +390,10 @@ class Pipeline:
             self.store_keys_e4m3(k, s.t_past, s.bcp)
         self.score(q, k)
         if self.n_rounds:
-            qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds,
-                            self.keep_latest, self.idx, self.ld_idx, self.sel_len, self.s_round,
-                            self.chosen)
+            flags = ((QK_ROUNDS_KEEP_LATEST if self.keep_latest else 0)
+                     | (QK_ROUNDS_SHARED if self.shared_rounds else 0))
+            qk_round_select(s, self.s_agg, self.n_rounds, round_off, self.top_rounds, flags,
+                            self.idx, self.ld_idx, self.sel_len, self.s_round, self.chosen)
         else:
             qk_topk(s.b * s.nkv, s.t_past, s.bsa, self.s_agg, self.s_agg.shape[-1], self.idx,
                     self.ld_idx, self.topk_ws, self.topk_ws_bytes)

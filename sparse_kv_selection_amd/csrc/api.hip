@@ -275,14 +275,18 @@ qk_status qk_round_select(const qk_shape* s, const float* s_agg, int32_t n_round
   if (st != QK_OK) return st;
   if (!s_agg || !round_off || !idx || !sel_len) return QK_ERR_NULL;
   if (n_rounds < 1 || n_rounds > 4096 || top_r < 1) return QK_ERR_SHAPE;
-  if (top_r + (keep_latest ? 1 : 0) > n_rounds) return QK_ERR_SHAPE;
+  const bool latest = (keep_latest & QK_ROUNDS_KEEP_LATEST) != 0;
+  const bool shared = (keep_latest & QK_ROUNDS_SHARED) != 0;
+  if (keep_latest & ~(QK_ROUNDS_KEEP_LATEST | QK_ROUNDS_SHARED)) return QK_ERR_UNSUPPORTED;
+  if (shared && !s_round) return QK_ERR_NULL;  // the heads' round scores meet there
+  if (top_r + (latest ? 1 : 0) > n_rounds) return QK_ERR_SHAPE;
   if (s->t_past < n_rounds || ld_idx < s->t_past) return QK_ERR_SHAPE;
   if (!aligned4(s_agg) || !aligned4(round_off) || !aligned4(idx) || !aligned4(sel_len) ||
       (s_round && !aligned4(s_round)))
     return QK_ERR_ALIGN;
   return hip_status(qk::launch_round_select(s_agg, s->b * s->nkv, s->t_past, n_rounds, round_off,
-                                            top_r, keep_latest ? 1 : 0, idx, ld_idx, sel_len,
-                                            s_round, chosen, hs(stream)));
+                                            top_r, latest ? 1 : 0, idx, ld_idx, sel_len,
+                                            s_round, chosen, shared ? s->nkv : 0, hs(stream)));
 }
 
 qk_status qk_gather(const qk_shape* s, const void* k, const void* v, const int32_t* idx,

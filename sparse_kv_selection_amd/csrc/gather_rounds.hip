@@ -80,6 +80,69 @@ __device__ int round_excl_scan(int v, int* wsum, int* total) {
   return off + x - v;
 }
 
+// Phases 2-4 of the round selection from the rounds' maxima rkey (order keys,
+// 0 = empty round) and the clamped bounds so: the chosen rounds, their output
+// offsets, their positions, then the per-round outputs.  Every thread of the
+// block calls this.
+__device__ void choose_rounds(const int* so, const uint32_t* rkey, int* base, int* wsum,
+                              int n_rounds, int top_r, int keep_latest, int bj,
+                              int32_t* __restrict__ idx, int ld_idx, int32_t* __restrict__ sel_len,
+                              float* __restrict__ s_round_out, uint8_t* __restrict__ chosen_out) {
+  const int tid = threadIdx.x;
+  // 2. chosen rounds by rank (ties: lower round id); the latest is always
+  //    kept.  kRankThreads threads count the better rounds of one round.
+  const int n_cand = keep_latest ? n_rounds - 1 : n_rounds;
+  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads / kRankThreads) {
+    const int r = r0 + tid / kRankThreads, part = tid % kRankThreads;
+    const int rr = r < n_rounds ? r : n_rounds - 1;
+    const float sr = rkey[rr] ? ofloat(rkey[rr]) : -INFINITY;
+    int better = 0;
+    if (rr < n_cand)
+      for (int r2 = part; r2 < n_cand; r2 += kRankThreads) {
+        const float s2 = rkey[r2] ? ofloat(rkey[r2]) : -INFINITY;
+        better += (s2 > sr) | ((s2 == sr) & (r2 < rr));
+      }
+    better = group_sum<kRankThreads>(better);
+    if (r < n_rounds && part == 0) base[r] = (rr >= n_cand || better < top_r) ? 1 : -1;
+  }
+  __syncthreads();
+
+  // 3. output offsets of the chosen rounds, in round order
+  int running = 0;
+  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads) {
+    const int r = r0 + tid;
+    const int len = (r < n_rounds && base[r] > 0) ? so[r + 1] - so[r] : 0;
+    int tot;
+    const int ex = round_excl_scan(len, wsum, &tot);
+    if (r < n_rounds) base[r] = base[r] > 0 ? running + ex : -1;
+    running += tot;
+  }
+  __syncthreads();
+
+  // 4. positions of the chosen rounds, ascending: the waves take the rounds
+  //    round-robin, and a chosen round's positions go out in coalesced stores
+  int32_t* out = idx + static_cast<size_t>(bj) * ld_idx;
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < n_rounds; r += kRoundWaves) {
+      const int b0 = base[r];
+      if (b0 < 0) continue;
+      for (int t = so[r] + lane; t < so[r + 1]; t += 64) {
+        const int o = b0 + (t - so[r]);
+        if (o < ld_idx) out[o] = t;
+      }
+    }
+  }
+  __syncthreads();
+  // per-round outputs last (a global store issued before a barrier holds the
+  // barrier until it completes); base[r] >= 0 marks a chosen round
+  for (int r = tid; r < n_rounds; r += kRoundThreads) {
+    if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
+    if (chosen_out) chosen_out[static_cast<size_t>(bj) * n_rounds + r] = base[r] >= 0 ? 1 : 0;
+  }
+  if (tid == 0) sel_len[bj] = min(running, ld_idx);
+}
+
 __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
     const float* __restrict__ s_agg, int t_past, int n_rounds, const int32_t* __restrict__ off,
     int top_r, int keep_latest, int32_t* __restrict__ idx, int ld_idx,
@@ -145,59 +208,35 @@ __global__ __launch_bounds__(kRoundThreads) void round_select_kernel(
     }
   }
   __syncthreads();
+  choose_rounds(so, rkey, base, wsum, n_rounds, top_r, keep_latest, bj, idx, ld_idx, sel_len,
+                s_round_out, chosen_out);
+}
 
-  // 2. chosen rounds by rank (ties: lower round id); the latest is always
-  //    kept.  kRankThreads threads count the better rounds of one round.
-  const int n_cand = keep_latest ? n_rounds - 1 : n_rounds;
-  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads / kRankThreads) {
-    const int r = r0 + tid / kRankThreads, part = tid % kRankThreads;
-    const int rr = r < n_rounds ? r : n_rounds - 1;
-    const float sr = rkey[rr] ? ofloat(rkey[rr]) : -INFINITY;
-    int better = 0;
-    if (rr < n_cand)
-      for (int r2 = part; r2 < n_cand; r2 += kRankThreads) {
-        const float s2 = rkey[r2] ? ofloat(rkey[r2]) : -INFINITY;
-        better += (s2 > sr) | ((s2 == sr) & (r2 < rr));
-      }
-    better = group_sum<kRankThreads>(better);
-    if (r < n_rounds && part == 0) base[r] = (rr >= n_cand || better < top_r) ? 1 : -1;
-  }
-  __syncthreads();
-
-  // 3. output offsets of the chosen rounds, in round order
-  int running = 0;
-  for (int r0 = 0; r0 < n_rounds; r0 += kRoundThreads) {
-    const int r = r0 + tid;
-    const int len = (r < n_rounds && base[r] > 0) ? so[r + 1] - so[r] : 0;
-    int tot;
-    const int ex = round_excl_scan(len, wsum, &tot);
-    if (r < n_rounds) base[r] = base[r] > 0 ? running + ex : -1;
-    running += tot;
-  }
-  __syncthreads();
-
-  // 4. positions of the chosen rounds, ascending: the waves take the rounds
-  //    round-robin, and a chosen round's positions go out in coalesced stores
-  int32_t* out = idx + static_cast<size_t>(bj) * ld_idx;
-  {
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < n_rounds; r += kRoundWaves) {
-      const int b0 = base[r];
-      if (b0 < 0) continue;
-      for (int t = so[r] + lane; t < so[r + 1]; t += 64) {
-        const int o = b0 + (t - so[r]);
-        if (o < ld_idx) out[o] = t;
-      }
-    }
-  }
-  __syncthreads();
-  // per-round outputs last (a global store issued before a barrier holds the
-  // barrier until it completes); base[r] >= 0 marks a chosen round
+// Round choice shared by the KV heads of a sequence: the round maxima of all
+// of the sequence's heads (written by round_select_kernel to s_round) meet in
+// one maximum per round, and every head gets the rounds chosen by it.  One
+// workgroup per (sequence, KV head), rewriting that head's index list,
+// length and chosen mask; s_round keeps the heads' own round scores.
+__global__ __launch_bounds__(kRoundThreads) void round_share_kernel(
+    int nkv, int t_past, int n_rounds, const int32_t* __restrict__ off, int top_r, int keep_latest,
+    int32_t* __restrict__ idx, int ld_idx, int32_t* __restrict__ sel_len,
+    const float* __restrict__ s_round, uint8_t* __restrict__ chosen_out) {
+  extern __shared__ int sm[];
+  int* so = sm;
+  uint32_t* rkey = reinterpret_cast<uint32_t*>(so + n_rounds + 1);
+  int* base = reinterpret_cast<int*>(rkey + n_rounds);
+  __shared__ int wsum[kRoundWaves];
+  const int tid = threadIdx.x;
+  const int bj = blockIdx.x, b = bj / nkv;
+  for (int r = tid; r <= n_rounds; r += kRoundThreads) so[r] = min(max(off[r], 0), t_past);
   for (int r = tid; r < n_rounds; r += kRoundThreads) {
-    if (s_round_out) s_round_out[static_cast<size_t>(bj) * n_rounds + r] = rkey[r] ? ofloat(rkey[r]) : -INFINITY;
-    if (chosen_out) chosen_out[static_cast<size_t>(bj) * n_rounds + r] = base[r] >= 0 ? 1 : 0;
+    float m = -INFINITY;
+    for (int j = 0; j < nkv; ++j) m = fmaxf(m, s_round[(static_cast<size_t>(b) * nkv + j) * n_rounds + r]);
+    rkey[r] = m == -INFINITY ? 0u : okey(m);
   }
-  if (tid == 0) sel_len[bj] = min(running, ld_idx);
+  __syncthreads();
+  choose_rounds(so, rkey, base, wsum, n_rounds, top_r, keep_latest, bj, idx, ld_idx, sel_len,
+                nullptr, chosen_out);
 }
 
 }  // namespace
@@ -220,10 +259,14 @@ hipError_t launch_gather(int esz, const void* k, const void* v, const int32_t* i
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,
                                const int32_t* off, int top_r, int keep_latest, int32_t* idx,
                                int ld_idx, int32_t* sel_len, float* s_round, uint8_t* chosen,
-                               hipStream_t st) {
+                               int shared_nkv, hipStream_t st) {
   const size_t shm = sizeof(int) * (3 * static_cast<size_t>(n_rounds) + 1);
   hipLaunchKernelGGL(round_select_kernel, dim3(bnkv), dim3(kRoundThreads), shm, st, s_agg, t_past,
                      n_rounds, off, top_r, keep_latest, idx, ld_idx, sel_len, s_round, chosen);
+  if (shared_nkv > 0)
+    hipLaunchKernelGGL(round_share_kernel, dim3(bnkv), dim3(kRoundThreads), shm, st, shared_nkv,
+                       t_past, n_rounds, off, top_r, keep_latest, idx, ld_idx, sel_len, s_round,
+                       chosen);
   return hipGetLastError();
 }
 

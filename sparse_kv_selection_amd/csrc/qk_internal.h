@@ -62,7 +62,7 @@ hipError_t launch_topk(int rows, int n, int k, const float* scores, int ld_score
 hipError_t launch_round_select(const float* s_agg, int bnkv, int t_past, int n_rounds,
                                const int32_t* off, int top_r, int keep_latest, int32_t* idx,
                                int ld_idx, int32_t* sel_len, float* s_round, uint8_t* chosen,
-                               hipStream_t st);
+                               int shared_nkv, hipStream_t st);
 
 // Row gather of selected K/V rows.
 hipError_t launch_gather(int esz, const void* k, const void* v, const int32_t* idx, int ld_idx,

@@ -89,7 +89,7 @@ def group_agreement(gpu_qidx, ref_qidx, G):
 # --------------------------------------------------------------------------
 def staged_selection(qn, kn, t_past, nq_keep, bsa, gpu_sq, gpu_qidx, gpu_s_agg, gpu_idx,
                      score="cosine", k_e4m3=False, round_off=None, top_rounds=0, gpu_sel_len=None,
-                     what=""):
+                     shared_rounds=False, what=""):
     """qn (b, nq, bcp, d), kn (b, nkv, >= t_past + bcp, d): fp64 inputs of the
     chunk; gpu_*: the GPU pipeline's outputs for the same sequences (numpy).
 
@@ -163,9 +163,14 @@ def staged_selection(qn, kn, t_past, nq_keep, bsa, gpu_sq, gpu_qidx, gpu_s_agg, 
                 got = np.unique(np.searchsorted(off, sel, side="right") - 1)
                 assert R - 1 in got, f"{what} b{bi} j{j}: latest round missing"
                 assert lens[bi, j] == sum(int(off[r + 1] - off[r]) for r in got), "partial rounds"
-                want = oracle.select_rounds(s_round[bi:bi + 1, j:j + 1], top_rounds)[0][0]
+                if shared_rounds:  # ranked by the maximum over the sequence's heads
+                    want = oracle.select_rounds_shared(s_round[bi:bi + 1], top_rounds)[0][j]
+                    rank_by = s_round[bi, :, :R - 1].max(axis=0)
+                else:
+                    want = oracle.select_rounds(s_round[bi:bi + 1, j:j + 1], top_rounds)[0][0]
+                    rank_by = s_round[bi, j, :R - 1]
                 swaps += assert_set_within_boundary(got[got != R - 1], want[want != R - 1],
-                                                    s_round[bi, j, :R - 1], top_rounds,
+                                                    rank_by, top_rounds,
                                                     what=f"{what} rounds b{bi} j{j}")
                 row.append(sel)
             key_sets.append(row)

@@ -162,6 +162,13 @@ def test_round_select_rejects():
     assert f(ctypes.byref(s), _p(), 8, _p(), 0, 1, _p(), 1000, _p(), None, None, None) == SHAPE
     assert f(ctypes.byref(s), _p(), 8, _p(), 2, 1, _p(), 999, _p(), None, None, None) == SHAPE
     assert f(ctypes.byref(s), _p(), 8, None, 2, 1, _p(), 1000, _p(), None, None, None) == NULL
+    # the head-shared choice needs s_round (the heads' round scores meet there);
+    # unknown flag bits are refused
+    assert f(ctypes.byref(s), _p(), 8, _p(), 2, qk.QK_ROUNDS_KEEP_LATEST | qk.QK_ROUNDS_SHARED,
+             _p(), 1000, _p(), None, None, None) == NULL
+    assert f(ctypes.byref(s), _p(), 8, _p(), 2, 4, _p(), 1000, _p(), None, None, None) == UNSUP
+    text = open(HEADER).read()
+    assert "#define QK_ROUNDS_KEEP_LATEST 1" in text and "#define QK_ROUNDS_SHARED 2" in text
 
 
 @nogpu

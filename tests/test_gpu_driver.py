@@ -118,17 +118,22 @@ def test_layer_stack_watershed_reuse(gpu):
     assert all(c.length == t_past + bcp for c in caches)
 
 
-def test_round_offload_matches_resident_stack(gpu):
+@pytest.mark.parametrize("shared", [False, True])
+def test_round_offload_matches_resident_stack(gpu, shared):
     """Upper layers held per round in host memory: every layer's output equals
     the resident stack's bit for bit; the copies are the rounds some KV head
-    chose, once per upper layer; the watershed's rounds agree with the
-    oracle's (near-tie swaps only) and the upper layers with the oracle's
-    attention over the GPU's key sets; the GPU holds fewer KV bytes."""
+    chose (with the shared choice: the same rounds for every head), once per
+    upper layer, into staging caches sized to them; the watershed's rounds
+    agree with the oracle's (near-tie swaps only; shared: exactly the
+    oracle's shared choice on the GPU's round scores) and the upper layers
+    with the oracle's attention over the GPU's key sets; the GPU holds fewer
+    KV bytes, by the rounds staged."""
     from sparse_kv_selection_amd import driver
     L, w, T, bcp, R, top = 5, 1, 3000, 128, 12, 3
     off = W.round_offsets(T, R, 11)
     layers = _sequence(T + bcp, 4001, layers=L)
-    stack = driver.RoundOffloadStack(L, w, off, 1, NKV, D_HEAD, bcp, device=_dev())
+    stack = driver.RoundOffloadStack(L, w, off, 1, NKV, D_HEAD, bcp, device=_dev(),
+                                     shared_rounds=shared)
     caches = []
     for layer, (q, k, v) in enumerate(layers):
         stack.load_history(layer, k, v)
@@ -143,24 +148,36 @@ def test_round_offload_matches_resident_stack(gpu):
     outs, pipe = stack.step(qs, krows, vrows, 16, top, bsa_plan=T // 4)
     off_dev = torch.tensor(off, dtype=torch.int32, device=_dev())
     outs_r, pipe_r = driver.layer_stack_step(qs, caches, krows, vrows, 16, T // 4, w,
-                                             round_off=off_dev, top_rounds=top)
+                                             round_off=off_dev, top_rounds=top,
+                                             shared_rounds=shared)
     torch.cuda.synchronize()
+    chosen = npi(pipe.chosen)
+    union = [r for r in range(R) if chosen[..., r].any()]
+    lens = np.diff(np.asarray(off))
+    staged = sum(int(lens[r]) for r in union)
+    # (the staged attention keeps the resident plan while the staging holds at
+    # least the plan's keys: then the outputs agree bit for bit)
+    assert staged >= T // 4
     for layer in range(L):
         assert torch.equal(outs[layer], outs_r[layer]), layer
     assert torch.equal(pipe.sel_len, pipe_r.sel_len)
-    chosen = npi(pipe.chosen)
-    union = [r for r in range(R) if chosen[..., r].any()]
     assert stack.last_rounds == union
-    lens = np.diff(np.asarray(off))
+    assert stack.last_staged == staged
     assert stack.last_h2d_bytes == (L - w - 1) * sum(2 * NKV * int(lens[r]) * D_HEAD * 2 for r in union)
-    assert stack.device_kv_bytes() < stack.resident_kv_bytes()
+    assert stack.staged_kv_bytes() < stack.resident_kv_bytes()
+    assert stack.staged_kv_bytes() == (w + 1) * 2 * NKV * (T + bcp) * D_HEAD * 2 + 2 * 2 * NKV * (staged + bcp) * D_HEAD * 2
+    if shared:
+        assert len(union) == top + 1 and all(np.array_equal(chosen[0, j], chosen[0, 0]) for j in range(NKV))
+        want = oracle.select_rounds_shared(np64(pipe.s_round), top)
+        assert all(np.flatnonzero(chosen[0, j]).tolist() == want[0][j].tolist() for j in range(NKV))
     # the watershed's rounds against the oracle's (the latest round is always kept)
     qn = [np64(x) for x in qs]
     kn = [np64(k) for (_, k, _) in layers]
     vn = [np64(v) for (_, _, v) in layers]
     sets, st = staged_selection(qn[w], kn[w], T, 16, T // 4, np64(pipe.sq), npi(pipe.q_idx),
                                 np64(pipe.s_agg), npi(pipe.idx), round_off=np.asarray(off),
-                                top_rounds=top, gpu_sel_len=npi(pipe.sel_len), what="watershed")
+                                top_rounds=top, gpu_sel_len=npi(pipe.sel_len),
+                                shared_rounds=shared, what="watershed")
     for j in range(NKV):   # the chosen-round mask names the same rounds as the index list
         rounds_in_list = np.unique(np.searchsorted(off, sets[0][j], side="right") - 1)
         assert np.array_equal(np.flatnonzero(chosen[0, j]), rounds_in_list)

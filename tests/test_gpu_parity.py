@@ -514,6 +514,40 @@ def test_sparse_equals_dense_at_full_budget(gpu):
 # round-granular selection
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name", list(ROUND_CASES))
+def test_round_select_shared(gpu, name):
+    """One round choice for all KV heads (QK_ROUNDS_SHARED) on the oracle's
+    fp32 scores: the heads' own round scores exactly, and the chosen mask,
+    lengths and position lists exactly the oracle's shared choice (maxima of
+    fp32 values are exact, so both sides rank the same numbers); every head
+    of a sequence gets the same rounds."""
+    qk = gpu
+    spec, case, ref, g = _case(name, ROUND_CASES)
+    s = _shape(spec, qk)
+    dev = _dev()
+    scores32 = ref["s_agg"].astype(np.float32)
+    idx = torch.full((s.b, s.nkv, s.t_past), -1, dtype=torch.int32, device=dev)
+    sel_len = torch.empty((s.b, s.nkv), dtype=torch.int32, device=dev)
+    s_round = torch.empty((s.b, s.nkv, spec.n_rounds), dtype=torch.float32, device=dev)
+    chosen_mask = torch.full((s.b, s.nkv, spec.n_rounds), 7, dtype=torch.uint8, device=dev)
+    qk.qk_round_select(s, torch.from_numpy(scores32).to(dev), spec.n_rounds, g["round_off"],
+                       spec.top_rounds, qk.QK_ROUNDS_KEEP_LATEST | qk.QK_ROUNDS_SHARED, idx,
+                       s.t_past, sel_len, s_round, chosen_mask)
+    torch.cuda.synchronize()
+    off = case["round_off"].numpy()
+    want_sr = oracle.round_scores(scores32.astype(np.float64), off)
+    assert np.array_equal(np64(s_round), want_sr)
+    chosen = oracle.select_rounds_shared(want_sr, spec.top_rounds)
+    sets = oracle.round_key_sets(chosen, off)
+    cm, gi, gl = npi(chosen_mask), npi(idx), npi(sel_len)
+    for b in range(s.b):
+        for j in range(s.nkv):
+            assert np.flatnonzero(cm[b, j]).tolist() == chosen[b][j].tolist()
+            assert np.array_equal(cm[b, j], cm[b, 0])
+            assert gl[b, j] == len(sets[b][j])
+            assert np.array_equal(gi[b, j, : gl[b, j]], sets[b][j])
+
+
+@pytest.mark.parametrize("name", list(ROUND_CASES))
 def test_round_select_and_attention(gpu, name):
     qk = gpu
     spec, case, ref, g = _case(name, ROUND_CASES)
