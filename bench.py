@@ -378,8 +378,15 @@ def main():
     stages = ((["store_keys"] if e4m3 else []) + ["qsel", "kvscore", "select", "attention"]
               + (["select_one_call"] if pipe.fused_select else []))
 
+    read_sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
     def run_stage(name, c):
-        if name == "store_keys":
+        if name == "read_keys":
+            # measurement only: the scoring pass's key loads with nothing
+            # computed (its floor over these bytes on this GPU)
+            qk.qk_calib_read_rate(shape, c["k8"] if e4m3 else c["k"],
+                                  qk.QK_KEYS_E4M3 if e4m3 else qk.QK_KEYS_DTYPE, read_sink)
+        elif name == "store_keys":
             qk.qk_keys_to_e4m3(shape, c["k"], spec.t_past, spec.bcp, c["k8"])
         elif name == "qsel":
             qk.qk_qsel(shape, c["q"], pipe.q_idx, pipe.sq, pipe.q_group)
@@ -408,7 +415,8 @@ def main():
 
     reps = max(10, args.steps)
     stage_ms = {}
-    for sname in stages:
+    read_floor = spec.dtype == "bf16"
+    for sname in stages + (["read_keys"] if read_floor else []):
         for i in range(2):
             run_stage(sname, inputs[i % copies])
         torch.cuda.synchronize()
@@ -419,6 +427,7 @@ def main():
         torch.cuda.synchronize()
         stage_ms[sname] = e0.elapsed_time(e1) / reps
 
+    read_ms = stage_ms.pop("read_keys", None)
     n_sel = float(pipe.sel_len.float().mean()) if rounds else float(shape.n_sel)
     work = algorithmic(spec, n_sel, key_bytes=1 if e4m3 else None)
     score_gbs = work["score_bytes"] / (stage_ms["kvscore"] * 1e-3) / 1e9
@@ -433,6 +442,13 @@ def main():
                   "traffic": None if variant else measured_traffic(spec.name, "kvscore"),
                   "algorithmic_bytes": work["score_bytes"],
                   "ms": round(stage_ms["kvscore"], 5)}
+    if read_ms:
+        # beside the published peak, the floor this GPU sets for these bytes:
+        # a bare read of the same keys in the pass's grid and ring
+        key_bytes = spec.b * spec.nkv * spec.t_past * spec.d * (1 if e4m3 else 2)
+        roof_score["ceiling"] = {"bare_read_ms": round(read_ms, 5),
+                                 "bare_read_gbps": round(key_bytes / (read_ms * 1e-3) / 1e9, 1),
+                                 "frac": round(read_ms / stage_ms["kvscore"], 4)}
     # the attention plan's choice: the eight-wave ping-pong kernel at d = 128
     # when a KV head has more than 128 query rows
     pp = spec.d == 128 and (spec.nq // spec.nkv) * spec.bcp > 128

@@ -338,6 +338,22 @@ qk_status qk_dense_attn(const qk_shape* s, const void* q, const void* k,
  * out: device, 256 * 512 floats (written, meaningless). */
 qk_status qk_calib_matrix_rate(int32_t mode, int32_t iters, float* out, qk_stream_t stream);
 
+/* Measurement only (no step of the method): a bare read of the keys a scoring
+ * pass reads for shape s (qk_kvscore_grouped, qk_kvscore_variant, qk_select's
+ * scoring) with the same grid, block order, lane layout and ring of blocks in
+ * flight, and nothing computed or stored.  Its duration is the floor of a
+ * scoring pass over these bytes on this GPU; a pass's time over this one's is
+ * the fraction of that floor it reaches.  k: device, (b, nkv, kv_cap, d) in
+ * the shape's dtype, or its one-byte E4M3 copy with key_format QK_KEYS_E4M3;
+ * rows [0, t_past) of each (b, KV head) are read.  sink: device, 16 bytes,
+ * 16-byte aligned, written only if the XOR of every word read equals a fixed
+ * sentinel (never in practice).  Errors: QK_ERR_NULL; QK_ERR_DTYPE for fp32
+ * shapes (the fp32 scoring pass has no ring); QK_ERR_UNSUPPORTED for another
+ * key_format or an NQ the bf16 scoring pass does not handle; QK_ERR_SHAPE,
+ * QK_ERR_ALIGN as for qk_kvscore_grouped.  t_past = 0 reads nothing. */
+qk_status qk_calib_read_rate(const qk_shape* s, const void* k, int32_t key_format, void* sink,
+                             qk_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ EXPORTED = ["qk_abi_version", "qk_status_string", "qk_workspace_bytes", "qk_qsel
             "qk_kvscore", "qk_kvscore_grouped", "qk_kvscore_variant", "qk_keys_to_e4m3",
             "qk_topk", "qk_select", "qk_round_select", "qk_gather", "qk_sparse_attn",
             "qk_sparse_attn_indexed", "qk_sparse_attn_indexed_noalloc", "qk_dense_attn",
-            "qk_calib_matrix_rate"]
+            "qk_calib_matrix_rate", "qk_calib_read_rate"]
 QK_NOALLOC_SCRATCH_BYTES = 20 << 20    # the fixed scratch array of qk_sparse_attn_indexed_noalloc
 
 
@@ -113,6 +113,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_sparse_attn_indexed_noalloc": ([F, P, P, P, P, I, P, P, P, P], I),
         "qk_dense_attn": ([F, P, P, P, P, P, P, SZ, P], I),
         "qk_calib_matrix_rate": ([I, I, P, P], I),
+        "qk_calib_read_rate": ([F, P, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -269,6 +270,13 @@ def qk_calib_matrix_rate(mode, iters, out, stream=None):
     near-constant or random operands (see include/qk.h)."""
     _check("qk_calib_matrix_rate", load_library().qk_calib_matrix_rate(int(mode), int(iters),
                                                                         _ptr(out), _stream(stream)))
+
+
+def qk_calib_read_rate(shape, k, key_format, sink, stream=None):
+    """Measurement only: a bare read of the keys a scoring pass reads for
+    `shape`, in its grid and ring, computing nothing (see include/qk.h)."""
+    _check("qk_calib_read_rate", load_library().qk_calib_read_rate(
+        _sh(shape), _ptr(k), int(key_format), _ptr(sink), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -201,6 +201,37 @@ qk_status qk_kvscore_variant(const qk_shape* s, const void* q, const int32_t* q_
                         mode == QK_SCORE_DOT);
 }
 
+qk_status qk_calib_read_rate(const qk_shape* s, const void* k, int32_t key_format, void* sink,
+                             qk_stream_t stream) {
+  qk_status st = check_shape(s);
+  if (st != QK_OK) return st;
+  if (!k || !sink) return QK_ERR_NULL;
+  if (key_format != QK_KEYS_DTYPE && key_format != QK_KEYS_E4M3) return QK_ERR_UNSUPPORTED;
+  if (!is_bf16(s)) return QK_ERR_DTYPE;
+  // the grid follows the scoring pass's, which depends on NQ
+  if (s->nq_keep < 1 || s->nq_keep > s->bcp) return QK_ERR_SHAPE;
+  if (s->nq_keep > (s->d == 256 ? 32 : 64)) return QK_ERR_UNSUPPORTED;
+  if (!aligned16(k) || !aligned16(sink)) return QK_ERR_ALIGN;
+  qk::ScoreCall c;
+  c.bf16 = true;
+  c.q_group = nullptr;
+  c.q = nullptr;
+  c.q_idx = nullptr;
+  c.k = k;
+  c.s_agg = nullptr;
+  c.b = s->b;
+  c.nq = s->nq;
+  c.nkv = s->nkv;
+  c.d = s->d;
+  c.bcp = s->bcp;
+  c.t_past = s->t_past;
+  c.kv_cap = s->kv_cap;
+  c.nq_keep = s->nq_keep;
+  c.k_e4m3 = key_format == QK_KEYS_E4M3;
+  c.read_sink = sink;
+  return hip_status(qk::launch_kvscore(c, hs(stream)));
+}
+
 qk_status qk_keys_to_e4m3(const qk_shape* s, const void* k, int32_t row0, int32_t nrows,
                           uint8_t* k8, qk_stream_t stream) {
   qk_status st = check_shape(s);

@@ -458,6 +458,47 @@ __global__ __launch_bounds__(64 * kScoreWaves, (score_waves_per_simd<D, NQB>()))
   }
 }
 
+// Measurement only: the scoring pass's key loads -- the same grid, block
+// order, lane layout and ring of blocks in flight -- with nothing computed.
+// The loaded words are folded by XOR; the fold reaches the sink only if it
+// equals a fixed sentinel, which keeps every load live while writing nothing
+// in practice.  Its duration is the floor of a scoring pass over these bytes.
+template <int D, int STAGES, bool FP8>
+__global__ __launch_bounds__(64 * kScoreWaves) void read_keys_kernel(ScoreArgs a, u32x4* sink) {
+  constexpr int NL = FP8 ? D / 32 : D / 16;  // 16-byte loads per key
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int bj = blockIdx.x / a.wgs_per_bj;
+  const int waves_per_bj = a.wgs_per_bj * kScoreWaves;
+  const int wi = (blockIdx.x - bj * a.wgs_per_bj) * kScoreWaves + wave;
+  const int nblk = wi < a.blocks_per_bj ? (a.blocks_per_bj - wi + waves_per_bj - 1) / waves_per_bj : 0;
+  auto block_of = [&](int m) { return wi + m * waves_per_bj; };
+  const char* kb = static_cast<const char*>(a.k) +
+                   (static_cast<size_t>(bj) * a.kv_cap * D + (FP8 ? 16 : 8) * half) * (FP8 ? 1 : 2);
+  u32x4 buf[STAGES][NL];
+  auto load_block = [&](int blk, u32x4* dst) {
+    const int row = min(blk * kBlock + col, a.kv_cap - 1);
+    const char* src = kb + static_cast<size_t>(row) * D * (FP8 ? 1 : 2);
+#pragma unroll
+    for (int s = 0; s < NL; ++s) dst[s] = ld16(src + 32 * s);
+  };
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i) load_block(block_of(i < nblk ? i : 0), buf[i]);
+  u32x4 fold = u32x4{0u, 0u, 0u, 0u};
+  for (int base = 0; base < nblk; base += STAGES) {
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i) {
+      const int m = base + i;
+      if (m >= nblk) break;
+      const int nxt = m + STAGES - 1;
+      if (nxt < nblk) load_block(block_of(nxt), buf[(i + STAGES - 1) % STAGES]);
+#pragma unroll
+      for (int s = 0; s < NL; ++s) fold ^= buf[i][s];
+    }
+  }
+  if ((fold[0] ^ fold[1] ^ fold[2] ^ fold[3]) == 0x5eed1e55u) *sink = fold;
+}
+
 // fp32 path: one thread per key, group queries staged in LDS (copied, or
 // formed from the kept queries as in the bf16 path: per (n, g) the inverse norm
 // of the kept row, then the mean of the normalised rows).
@@ -566,7 +607,16 @@ void launch_bf16(const ScoreCall& c, hipStream_t st) {
   // Blocks kept in flight per wave.  A wave with few blocks to score (short
   // rows) does better with a shallower ring (measured at d = 128: 3 for up to
   // 4 blocks per wave, 4 beyond).
-  if (D == 128 && NQB == 1 && bpw <= 4) launch_grid<D, NQB, 3>(a, c.k_e4m3, c.dot, grid, st);
+  const bool shallow = D == 128 && NQB == 1 && bpw <= 4;
+  if (c.read_sink) {
+    u32x4* sink = static_cast<u32x4*>(c.read_sink);
+    if (shallow && c.k_e4m3) hipLaunchKernelGGL((read_keys_kernel<D, 3, true>), grid, dim3(64 * kScoreWaves), 0, st, a, sink);
+    else if (shallow) hipLaunchKernelGGL((read_keys_kernel<D, 3, false>), grid, dim3(64 * kScoreWaves), 0, st, a, sink);
+    else if (c.k_e4m3) hipLaunchKernelGGL((read_keys_kernel<D, 4, true>), grid, dim3(64 * kScoreWaves), 0, st, a, sink);
+    else hipLaunchKernelGGL((read_keys_kernel<D, 4, false>), grid, dim3(64 * kScoreWaves), 0, st, a, sink);
+    return;
+  }
+  if (shallow) launch_grid<D, NQB, 3>(a, c.k_e4m3, c.dot, grid, st);
   else launch_grid<D, NQB, 4>(a, c.k_e4m3, c.dot, grid, st);
 }
 

@@ -37,6 +37,9 @@ struct ScoreCall {
   // t_past + bcp) the pass also stores as E4M3 codes into conv_dst
   const void* conv_src = nullptr;
   uint8_t* conv_dst = nullptr;
+  // measurement only (bf16): when set, the launch reads the keys with the
+  // scoring grid and ring but computes nothing (16-byte sink, see the kernel)
+  void* read_sink = nullptr;
 };
 hipError_t launch_kvscore(const ScoreCall& c, hipStream_t st);
 

@@ -120,6 +120,23 @@ def test_scoring_variants_reject():
 
 
 @nogpu
+def test_read_calibration_rejects():
+    lib = qk.load_library()
+    s = _shape()
+    f = lib.qk_calib_read_rate
+    assert f(None, _p(), 0, _p(), None) == NULL
+    assert f(ctypes.byref(s), None, 0, _p(), None) == NULL
+    assert f(ctypes.byref(s), _p(), 0, None, None) == NULL
+    assert f(ctypes.byref(s), _p(), 2, _p(), None) == UNSUP                    # key format
+    assert f(ctypes.byref(_shape(dtype=qk.QK_F32)), _p(), 0, _p(), None) == DTYPE
+    assert f(ctypes.byref(_shape(nq_keep=0)), _p(), 0, _p(), None) == SHAPE
+    assert f(ctypes.byref(_shape(nq_keep=33, d=256)), _p(), 0, _p(), None) == UNSUP
+    assert f(ctypes.byref(s), _p(FAKE + 8), 0, _p(), None) == ALIGN
+    assert f(ctypes.byref(s), _p(), 1, _p(FAKE + 4), None) == ALIGN
+    assert f(ctypes.byref(_shape(d=96)), _p(), 0, _p(), None) == UNSUP
+
+
+@nogpu
 def test_kvscore_limits():
     lib = qk.load_library()
     assert lib.qk_kvscore(ctypes.byref(_shape(nq_keep=65, bcp=128, kv_cap=2000)), _p(), _p(), _p(), None) == UNSUP
