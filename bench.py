@@ -40,16 +40,16 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 # followed by the shared device header): once either changes, the figure no
 # longer describes the kernel and `traffic` is null.
 MEASURED_TRAFFIC = {
-    ("llama3b_32k", "kvscore"): ("kvscore.hip", "e830876f7c0d3847", 70639958),
-    ("llama3b_32k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 72441812),
-    ("long_128k", "kvscore"): ("kvscore.hip", "e830876f7c0d3847", 278003712),
-    ("long_128k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 123568240),
-    ("decode_64x16k", "kvscore"): ("kvscore.hip", "e830876f7c0d3847", 2182209773),
-    ("decode_64x16k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 542617148),
-    ("rounds_64k", "kvscore"): ("kvscore.hip", "e830876f7c0d3847", 138844528),
-    ("rounds_64k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 95242288),
-    ("long_128k_d256", "kvscore"): ("kvscore.hip", "e830876f7c0d3847", 550335168),
-    ("long_128k_d256", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 173054000),
+    ("llama3b_32k", "kvscore"): ("kvscore.hip", "72bf584754d139ff", 70642998),
+    ("llama3b_32k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 72463144),
+    ("long_128k", "kvscore"): ("kvscore.hip", "72bf584754d139ff", 278068841),
+    ("long_128k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 123568384),
+    ("decode_64x16k", "kvscore"): ("kvscore.hip", "72bf584754d139ff", 2182091634),
+    ("decode_64x16k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 542617118),
+    ("rounds_64k", "kvscore"): ("kvscore.hip", "72bf584754d139ff", 138900976),
+    ("rounds_64k", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 95261832),
+    ("long_128k_d256", "kvscore"): ("kvscore.hip", "72bf584754d139ff", 550305161),
+    ("long_128k_d256", "attention"): ("attention.hip", "7b63cf47e9fab0a3", 173053928),
 }
 
 
