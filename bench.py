@@ -308,7 +308,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
-              "(each KV head or sequence would shard with no exchange; see the design notes).",
+              "(KV heads and sequences are independent: each GPU would take its own with no exchange).",
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
