@@ -127,3 +127,30 @@ def test_full_size_select_equals_separate_calls(gpu, name):
             assert torch.equal(x, y)
     want = oracle.select_keys(np64(a.s_agg), s.bsa)
     assert np.array_equal(npi(a.idx)[..., :want.shape[-1]], want)
+
+
+def test_million_key_row(gpu):
+    """A row eight times the longest workload's: one KV head of 8 query heads
+    over 2^20 past keys, a 64-row chunk, NQ = 16, BSA = 16384.  The scoring
+    grid runs 512 workgroups, the top-k 128 tiles of 8192 scores, the
+    attention its cap of 64 key splits.  Staged comparison of every KV group,
+    row and head, and the exact top-BSA of the GPU's own scores."""
+    qk = gpu
+    dev = torch.device("cuda:0")
+    spec = W.spec("long_128k", b=1, nq=8, nkv=1, t_past=1 << 20, bcp=64, nq_keep=16, bsa=16384)
+    print("[full-size] 1M-key row seed 1201", flush=True)
+    case = W.make_case(spec, 1201, device=dev)
+    q, k, v = case["q"], case["k"], case["v"]
+    s = qk.shape_of(spec)
+    pipe = qk.Pipeline(s, device=dev)
+    assert pipe.fused_select
+    pipe(q, k, v)
+    torch.cuda.synchronize()
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    sets, st = staged_selection(qn, kn, spec.t_past, spec.nq_keep, spec.bsa, np64(pipe.sq),
+                                npi(pipe.q_idx), np64(pipe.s_agg), npi(pipe.idx), what="1M row")
+    err = staged_attention(qn, kn, vn, spec.t_past, sets, pipe.out, spec.dtype,
+                           gpu_lse=pipe.lse, what="1M row")
+    want = oracle.select_keys(np64(pipe.s_agg), spec.bsa)
+    assert np.array_equal(npi(pipe.idx)[..., :want.shape[-1]], want)
+    print(f"[full-size] 1M-key row: {st}, attention err {err:.2e} (every row and head)", flush=True)
