@@ -35,6 +35,8 @@ CASES = {
     "f32_d128": ("tiny_f32", dict(d=128, t_past=777, bcp=45, nq_keep=9, bsa=300), 9),
     "long_chunk": ("llama3b_32k", dict(nq=6, nkv=2, t_past=1500, bcp=700, nq_keep=44, bsa=400), 10),
     "chunk_300": ("llama3b_32k", dict(nq=4, nkv=2, t_past=900, bcp=300, nq_keep=37, bsa=200), 11),
+    # a batch of prefill chunks: per-sequence rows, row tiles and key splits
+    "batch_prefill": ("llama3b_32k", dict(b=3, t_past=3000, bcp=128, bsa=700), 12),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
@@ -42,6 +44,9 @@ ROUND_CASES = {
     # rounds shorter than 256 positions on average: the per-thread scan
     "rounds_short": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=48,
                                         top_rounds=6), 1006),
+    # two sequences: rounds chosen (and shared by the heads) per sequence
+    "rounds_batch": ("rounds_64k", dict(b=2, nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
+                                        top_rounds=4), 1007),
 }
 
 _cache = {}
@@ -314,7 +319,7 @@ def test_pipeline_variants_end_to_end(gpu, name, mode, e4m3):
 
 
 SELECT_CASES = ["llama_ragged", "d256_small", "decode_small", "tiny_f32", "g1_all_keys",
-                "d64_nq40"]
+                "d64_nq40", "batch_prefill"]
 
 
 # 8-bit keys are scored with bf16 queries only (the API rejects fp32 + E4M3)
