@@ -37,6 +37,8 @@ CASES = {
     "chunk_300": ("llama3b_32k", dict(nq=4, nkv=2, t_past=900, bcp=300, nq_keep=37, bsa=200), 11),
     # a batch of prefill chunks: per-sequence rows, row tiles and key splits
     "batch_prefill": ("llama3b_32k", dict(b=3, t_past=3000, bcp=128, bsa=700), 12),
+    # a cache with spare rows after the chunk (kv_cap > T + bcp: every stride)
+    "cache_slack": ("llama3b_32k", dict(b=2, t_past=2500, bcp=96, bsa=600, kv_extra=333), 13),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
@@ -319,7 +321,7 @@ def test_pipeline_variants_end_to_end(gpu, name, mode, e4m3):
 
 
 SELECT_CASES = ["llama_ragged", "d256_small", "decode_small", "tiny_f32", "g1_all_keys",
-                "d64_nq40", "batch_prefill"]
+                "d64_nq40", "batch_prefill", "cache_slack"]
 
 
 # 8-bit keys are scored with bf16 queries only (the API rejects fp32 + E4M3)
