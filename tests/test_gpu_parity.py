@@ -39,6 +39,8 @@ CASES = {
     "batch_prefill": ("llama3b_32k", dict(b=3, t_past=3000, bcp=128, bsa=700), 12),
     # a cache with spare rows after the chunk (kv_cap > T + bcp: every stride)
     "cache_slack": ("llama3b_32k", dict(b=2, t_past=2500, bcp=96, bsa=600, kv_extra=333), 13),
+    # a past shorter than one key tile: scoring waves without blocks, one partial tile
+    "tiny_past": ("llama3b_32k", dict(nq=8, nkv=2, t_past=37, bcp=40, nq_keep=8, bsa=9), 14),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
@@ -321,7 +323,7 @@ def test_pipeline_variants_end_to_end(gpu, name, mode, e4m3):
 
 
 SELECT_CASES = ["llama_ragged", "d256_small", "decode_small", "tiny_f32", "g1_all_keys",
-                "d64_nq40", "batch_prefill", "cache_slack"]
+                "d64_nq40", "batch_prefill", "cache_slack", "tiny_past"]
 
 
 # 8-bit keys are scored with bf16 queries only (the API rejects fp32 + E4M3)
