@@ -41,6 +41,9 @@ CASES = {
     "cache_slack": ("llama3b_32k", dict(b=2, t_past=2500, bcp=96, bsa=600, kv_extra=333), 13),
     # a past shorter than one key tile: scoring waves without blocks, one partial tile
     "tiny_past": ("llama3b_32k", dict(nq=8, nkv=2, t_past=37, bcp=40, nq_keep=8, bsa=9), 14),
+    # decode steps at the other head dims
+    "decode_d256": ("long_128k_d256", dict(b=4, bcp=1, nq_keep=1, t_past=3000, bsa=500), 15),
+    "decode_d64": ("llama3b_32k", dict(d=64, b=4, bcp=1, nq_keep=1, t_past=2000, bsa=300), 16),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
