@@ -284,7 +284,8 @@ qk_status qk_gather(const qk_shape* s, const void* k, const void* v,
  *   out[b,h,i] = sum_key softmax(scale q.key) value;  lse = log sum exp(scale q.key)
  * k_sel, v_sel: (b,nkv,ld_sel,d); sel_len as in qk_gather; lse: (b,nq,bcp) f32
  * or NULL.  bf16: matrix-core products, fp32 softmax and accumulation; f32:
- * fp32 throughout.  Scratch: qk_workspace_bytes(QK_OP_SPARSE_ATTN). */
+ * fp32 throughout, d = 64 or 128 (f32 at d = 256: QK_ERR_UNSUPPORTED, as for
+ * every attention call).  Scratch: qk_workspace_bytes(QK_OP_SPARSE_ATTN). */
 qk_status qk_sparse_attn(const qk_shape* s, const void* q, const void* k_sel,
                          const void* v_sel, int32_t ld_sel, const int32_t* sel_len,
                          const void* k, const void* v, void* out, float* lse,

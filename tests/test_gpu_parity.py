@@ -44,6 +44,8 @@ CASES = {
     # decode steps at the other head dims
     "decode_d256": ("long_128k_d256", dict(b=4, bcp=1, nq_keep=1, t_past=3000, bsa=500), 15),
     "decode_d64": ("llama3b_32k", dict(d=64, b=4, bcp=1, nq_keep=1, t_past=2000, bsa=300), 16),
+    # the fp32 kernels at decode (no outlier queries: the chunk is one query)
+    "f32_decode": ("tiny_f32", dict(b=3, bcp=1, nq_keep=1, t_past=777, bsa=100, n_outliers=0), 17),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
