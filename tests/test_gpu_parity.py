@@ -46,6 +46,10 @@ CASES = {
     "decode_d64": ("llama3b_32k", dict(d=64, b=4, bcp=1, nq_keep=1, t_past=2000, bsa=300), 16),
     # the fp32 kernels at decode (no outlier queries: the chunk is one query)
     "f32_decode": ("tiny_f32", dict(b=3, bcp=1, nq_keep=1, t_past=777, bsa=100, n_outliers=0), 17),
+    # extremes: one kept query in a prefill chunk, one selected key, G = 64
+    "nq1_prefill": ("llama3b_32k", dict(nq=4, nkv=2, t_past=1200, bcp=50, nq_keep=1, bsa=150), 19),
+    "bsa1": ("llama3b_32k", dict(nq=4, nkv=2, t_past=800, bcp=40, nq_keep=8, bsa=1), 20),
+    "g64": ("llama3b_32k", dict(nq=64, nkv=1, t_past=900, bcp=16, nq_keep=8, bsa=200), 21),
 }
 ROUND_CASES = {
     "rounds_small": ("rounds_64k", dict(nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
