@@ -60,6 +60,11 @@ ROUND_CASES = {
     # two sequences: rounds chosen (and shared by the heads) per sequence
     "rounds_batch": ("rounds_64k", dict(b=2, nq=8, nkv=2, t_past=6000, bcp=128, n_rounds=16,
                                         top_rounds=4), 1007),
+    # every round chosen (top_r + latest = n_rounds); 400 rounds of 2-27 positions
+    "rounds_all": ("rounds_64k", dict(nq=8, nkv=2, t_past=3000, bcp=64, n_rounds=5,
+                                      top_rounds=4), 1008),
+    "rounds_many": ("rounds_64k", dict(nq=8, nkv=2, t_past=3000, bcp=64, n_rounds=400,
+                                       top_rounds=20), 1009),
 }
 
 _cache = {}
